@@ -1,0 +1,51 @@
+"""The fused producer: residual add -> Gemma RMSNorm -> per-token e4m3 quant.
+
+Test infrastructure (see the package docstring); never used by the product path.
+
+Source: radiance_arnq.py page (module docstring and ``ar_add_rms_quant``): each
+row-parallel output is finished by one kernel that adds the residual, applies
+the Gemma RMSNorm of the next layer's input norm and quantizes per token to
+e4m3, returning (q [M,K] e4m3, scale [M] fp32, residual_out [M,K]).  The norm
+is x * rsqrt(mean(x^2) + eps) * (1 + w) (Gemma's offset weight).  The quant
+step is the radiance_mxfp4.py page's per-token quant (see quant.py).
+
+Steps, in the pages' order, with the readings this oracle takes:
+  1. r = bf16(y + residual): the exact sum rounded once to bf16 (round to
+     nearest even); r is the residual-stream value both consumers see and is
+     returned bit for bit.
+  2. ms = mean_k r[k]^2, in fp64 over the bf16-rounded r.
+  3. inv = 1 / sqrt(ms + eps).
+  4. h = r * inv * (1 + w), fp64, w decoded from bf16.  No intermediate
+     rounding of h to bf16 (the fused op emits no bf16 hidden tensor).
+  5. the quant takes h as fp32, as the page's traced quant takes its input:
+     h32 = fp32(h); amax = max_k |h32|; scale = fp32(max(amax/448, 1/(448*512)))
+     (one rounding of the exact quotient).
+  6. q = e4m3(clamp(h32 / scale, +-448)), the division in fp32 as on the
+     page's traced quant, rounded to nearest even.
+A row of zeros gives h = 0, scale = 1/(448*512) and q = 0.  NaN/Inf inputs
+propagate (they are never generated).
+"""
+import numpy as np
+
+from .codecs import decode_bf16, round_to_bf16
+from .quant import scale_from_amax, quant_with_scale
+
+
+def add_rms_quant(y_bits, res_bits, w_bits, eps=1e-6, return_h=False):
+    """y, residual bf16 [M, K]; w bf16 [K] -> (q uint8 [M,K], scale fp32 [M],
+    residual_out bf16 [M,K]) and, on request, h fp64 [M,K]."""
+    y = decode_bf16(y_bits)
+    res = decode_bf16(res_bits)
+    w = decode_bf16(w_bits)
+    M, K = y.shape
+    r_bits = round_to_bf16(y + res)                               # step 1
+    r = decode_bf16(r_bits)
+    ms = np.mean(r * r, axis=1, keepdims=True)                    # step 2
+    inv = 1.0 / np.sqrt(ms + eps)                                 # step 3
+    h = r * inv * (1.0 + w)[None, :]                              # step 4
+    h32 = h.astype(np.float32)
+    s = scale_from_amax(np.abs(h32).astype(np.float64).max(axis=1))   # step 5
+    q = quant_with_scale(h32, s[:, None])                         # step 6
+    if return_h:
+        return q, s, r_bits, h
+    return q, s, r_bits
