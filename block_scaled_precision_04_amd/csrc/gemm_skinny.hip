@@ -1,0 +1,120 @@
+// Skinny bf16 NT GEMM C[M,N] = x[M,K] . W[N,K]^T for sub-megabyte weights at
+// M <= 64 (radiance_gemm.py page: gemm_bf16_nt_m64).  The page's diagnosis:
+// a weight under 1 MB gives a library GEMM only a handful of workgroups, each
+// walking all of K, so the GPU idles; its fix is heavy split-K (the measured
+// best MoE-gate config splits each column tile 16 ways) with a flat cost in M,
+// and its fallback splits K across workgroups through an fp32 partial slab and
+// per-tile counters.
+//
+// Here: grid = (N/16 column tiles, KSPLIT), four waves per workgroup, one
+// 128-wide K chunk per wave.  Each lane loads 64 contiguous bytes of a weight
+// row and of each activation row (four 16x16x32 bf16 MFMAs' worth; both
+// operands use the same K order so the products pair exactly), the four waves
+// reduce through LDS, and when K is split over several workgroups the partial
+// tile goes to the workspace slab; the last workgroup to finish a tile (an
+// atomic counter) sums the KSPLIT partials in index order (deterministic),
+// writes bf16 and resets the counter to zero for the next call.
+#include "common.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kChunk = 128;  // K per wave
+
+BS_INLINE v8bf as_bf(uint4 x) {
+  v4i t{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+  return __builtin_bit_cast(v8bf, t);
+}
+
+template <int MB>
+__global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                uint16_t* __restrict__ c, int M, int N, int K,
+                                                float* __restrict__ slab, int* __restrict__ counters) {
+  __shared__ float red[kWaves][MB * 4][64];
+  __shared__ int last;
+  const int nt = blockIdx.x, kb = blockIdx.y, ksplit = gridDim.y;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int chunk = kb * kWaves + wave;
+  v4f acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0, 0, 0, 0};
+  if (chunk * kChunk < K) {
+    const int k0 = chunk * kChunk + 32 * (l >> 4);
+    const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(nt * 16 + (l & 15)) * K + k0);
+    uint4 wv[4], xv[MB][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wv[j] = wr[j];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = 16 * mb + (l & 15);
+      const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[mb][j] = m < M ? xr[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(wv[j]), as_bf(xv[mb][j]), acc[mb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][mb * 4 + r][l] = acc[mb][r];
+  __syncthreads();
+  // Thread o of the workgroup owns output o = (mb, r, lane): m = 16mb + lane%16, n = 4(lane/16) + r.
+  for (int o = threadIdx.x; o < MB * 256; o += 256) {
+    const int lane = o & 63, rr = (o >> 6) & 3, mb = o >> 8;
+    float s = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) s += red[v][mb * 4 + rr][lane];
+    const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
+    if (ksplit == 1) {
+      if (m < M) c[m * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
+    } else if (m < M) {
+      slab[(static_cast<size_t>(kb) * M + m) * N + n] = s;
+    }
+  }
+  if (ksplit == 1) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(&counters[nt], 1) == ksplit - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int o = threadIdx.x; o < M * 16; o += 256) {
+    const int m = o >> 4, n = nt * 16 + (o & 15);
+    float s = 0.0f;
+    for (int b = 0; b < ksplit; ++b) s += __builtin_nontemporal_load(&slab[(static_cast<size_t>(b) * M + m) * N + n]);
+    c[m * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
+  }
+  if (threadIdx.x == 0) counters[nt] = 0;
+}
+
+}  // namespace
+
+int bs_skinny_ksplit(int K) { return (K / kChunk + kWaves - 1) / kWaves; }
+
+size_t bs_skinny_workspace(int M, int N, int K) {
+  const int ks = bs_skinny_ksplit(K);
+  if (ks <= 1) return 0;
+  const size_t slab = static_cast<size_t>(ks) * M * N * sizeof(float);
+  return (slab + 255) / 256 * 256 + static_cast<size_t>(N / 16) * sizeof(int);
+}
+
+int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
+                     hipStream_t st) {
+  const int ks = bs_skinny_ksplit(K);
+  float* slab = nullptr;
+  int* counters = nullptr;
+  if (ks > 1) {
+    slab = static_cast<float*>(ws);
+    const size_t off = (static_cast<size_t>(ks) * M * N * sizeof(float) + 255) / 256 * 256;
+    counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
+  }
+  dim3 grid(N / 16, ks);
+  if (M <= 16) k_skinny<1><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);
+  else if (M <= 32) k_skinny<2><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);
+  else k_skinny<4><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);
+  return bs_launch_status();
+}

@@ -1,0 +1,262 @@
+// Producers of e4m3 activations / weights for the block-scaled GEMMs.
+//
+// add_rms_quant_fp8: residual add -> Gemma RMSNorm -> per-token e4m3 quant in
+// one pass over HBM (radiance_arnq.py page: ar_add_rms_quant and the fp8
+// residual-stream contract; the quant rule is the radiance_mxfp4.py page's
+// _traced_quant: scale = max(rowamax/448, 1/(448*512)), fp32 math, clamp,
+// round-to-nearest cast).
+//
+// One 256-thread workgroup per row.  Each thread owns NC chunks of 8 bf16
+// (16-byte loads), keeps them in registers between the two row reductions
+// (sum of squares, then absolute maximum) and writes the e4m3 codes, so every
+// byte is read once and written once: 7 bytes per element plus 2 per column
+// of gamma (shared by all rows, cache-resident).
+//
+// Precision: r = bf16(y + residual) is exact (an fp32 add of two bf16 values
+// is exact or below half a bf16 ulp, so one more rounding to bf16 equals a
+// single rounding of the exact sum).  The sum of r^2 and the normalisation
+// are carried in fp64 and h is rounded once to fp32, so h, the row maximum
+// and the scale agree with a correctly rounded evaluation; the code decision
+// h/scale is an IEEE fp32 division followed by the hardware's round-to-
+// nearest-even e4m3 convert, as the page's traced quant takes it in fp32.
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+BS_INLINE float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+BS_INLINE double block_sum_f64(double v, double* red) {
+  v = wave_sum_f64(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  double r = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return r;
+}
+
+BS_INLINE uint2 quant8(const float* h, float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    float a = fminf(fmaxf(h[j] / s, -kFp8Max), kFp8Max);
+    float b = fminf(fmaxf(h[j + 1] / s, -kFp8Max), kFp8Max);
+    lo |= f32x2_to_e4m3(a, b) << (8 * j);
+  }
+#pragma unroll
+  for (int j = 4; j < 8; j += 2) {
+    float a = fminf(fmaxf(h[j] / s, -kFp8Max), kFp8Max);
+    float b = fminf(fmaxf(h[j + 1] / s, -kFp8Max), kFp8Max);
+    hi |= f32x2_to_e4m3(a, b) << (8 * (j - 4));
+  }
+  return make_uint2(lo, hi);
+}
+
+BS_INLINE void unpack8(uint4 v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// NORM = true: add + RMSNorm + quant.  NORM = false: per-token quant of y.
+template <int NC, bool NORM>
+__global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict__ y,
+                                                        const uint4* __restrict__ res,
+                                                        const uint4* __restrict__ gamma, float eps,
+                                                        uint2* __restrict__ q, float* __restrict__ scale,
+                                                        uint4* __restrict__ rout, int K) {
+  __shared__ double red_d[4];
+  __shared__ float red_f[4];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nch = K >> 3;
+  const size_t base = static_cast<size_t>(row) * nch;
+  float h[NC][8];
+  double ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = c * kThreads + t;
+    if (idx < nch) {
+      float a[8];
+      unpack8(y[base + idx], a);
+      if constexpr (NORM) {
+        float b[8];
+        unpack8(res[base + idx], b);
+        uint32_t rb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          rb[j] = f32_to_bf16_rne(a[j] + b[j]);
+          h[c][j] = __uint_as_float(rb[j] << 16);
+          ss += static_cast<double>(h[c][j]) * static_cast<double>(h[c][j]);
+        }
+        rout[base + idx] = make_uint4(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16),
+                                      rb[4] | (rb[5] << 16), rb[6] | (rb[7] << 16));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[c][j] = a[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[c][j] = 0.0f;
+    }
+  }
+  if constexpr (NORM) {
+    const double tot = block_sum_f64(ss, red_d);
+    const double inv = 1.0 / sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = c * kThreads + t;
+      if (idx < nch) {
+        float g[8];
+        unpack8(gamma[idx], g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          h[c][j] = static_cast<float>(static_cast<double>(h[c][j]) * inv * (1.0 + static_cast<double>(g[j])));
+      }
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
+  amax = block_max(amax, red_f);
+  const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+  if (t == 0) scale[row] = s;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = c * kThreads + t;
+    if (idx < nch) q[base + idx] = quant8(h[c], s);
+  }
+}
+
+// One scale per 128-wide group of each row.  Block = 256 threads = 16 groups
+// of 16 threads, each thread one 8-element chunk.  grid = (ceil(K/2048), M).
+__global__ __launch_bounds__(kThreads) void k_group_quant(const uint4* __restrict__ x, uint2* __restrict__ q,
+                                                          float* __restrict__ scale, int K) {
+  const int row = blockIdx.y;
+  const int nch = K >> 3;
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  const bool live = idx < nch;  // K % 128 == 0: whole 16-thread groups are live or not
+  float h[8];
+  if (live) {
+    unpack8(x[static_cast<size_t>(row) * nch + idx], h);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+  if (live) {
+    if ((threadIdx.x & 15) == 0) scale[static_cast<size_t>(row) * (K >> 7) + (idx >> 4)] = s;
+    q[static_cast<size_t>(row) * nch + idx] = quant8(h, s);
+  }
+}
+
+// One scale per 128x128 block of a weight.  One workgroup per block; thread t
+// handles row (t >> 1) of the block, chunks 8*(t&1) .. +8.
+__global__ __launch_bounds__(kThreads) void k_block_quant(const uint4* __restrict__ w, uint2* __restrict__ q,
+                                                          float* __restrict__ scale, int K) {
+  __shared__ float red_f[4];
+  const int bk = blockIdx.x, bn = blockIdx.y;
+  const int nch = K >> 3;
+  const int r = bn * 128 + (threadIdx.x >> 1);
+  const int c0 = bk * 16 + (threadIdx.x & 1) * 8;
+  float h[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    unpack8(w[static_cast<size_t>(r) * nch + c0 + c], h[c]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
+  }
+  amax = block_max(amax, red_f);
+  const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+  if (threadIdx.x == 0) scale[static_cast<size_t>(bn) * (K >> 7) + bk] = s;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) q[static_cast<size_t>(r) * nch + c0 + c] = quant8(h[c], s);
+}
+
+template <bool NORM>
+int launch_row_quant(const void* y, const void* res, const void* gamma, float eps, void* q, float* scale,
+                     void* rout, int M, int K, hipStream_t st) {
+  const int nc = (K / 8 + kThreads - 1) / kThreads;
+  dim3 grid(M), block(kThreads);
+#define BS_ROWQ(N_)                                                                                    \
+  k_row_quant<N_, NORM><<<grid, block, 0, st>>>(                                                        \
+      static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
+      static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
+  if (nc <= 1) BS_ROWQ(1);
+  else if (nc <= 2) BS_ROWQ(2);
+  else if (nc <= 3) BS_ROWQ(3);
+  else if (nc <= 4) BS_ROWQ(4);
+  else if (nc <= 6) BS_ROWQ(6);
+  else if (nc <= 8) BS_ROWQ(8);
+  else if (nc <= 12) BS_ROWQ(12);
+  else BS_ROWQ(16);
+#undef BS_ROWQ
+  return bs_launch_status();
+}
+
+constexpr int kMaxRowK = 32768;  // 16 chunks of 8 per thread
+
+}  // namespace
+
+extern "C" {
+
+BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* gamma, float eps, void* q,
+                             float* scale, void* residual_out, int M, int K, bs_stream_t stream) {
+  BS_CHECK(y && residual && gamma && q && scale && residual_out, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && K >= 8 && K % 8 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(y, 16) && bs_aligned(residual, 16) && bs_aligned(gamma, 16) && bs_aligned(q, 8) &&
+               bs_aligned(scale, 4) && bs_aligned(residual_out, 16),
+           BS_ERR_ALIGN);
+  BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
+  return launch_row_quant<true>(y, residual, gamma, eps, q, scale, residual_out, M, K,
+                                static_cast<hipStream_t>(stream));
+}
+
+BS_API int quant_fp8_per_token(const void* x, void* q, float* scale, int M, int K, bs_stream_t stream) {
+  BS_CHECK(x && q && scale, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && K >= 8 && K % 8 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(x, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);
+  return launch_row_quant<false>(x, nullptr, nullptr, 0.0f, q, scale, nullptr, M, K,
+                                 static_cast<hipStream_t>(stream));
+}
+
+BS_API int quant_fp8_group128(const void* x, void* q, float* scale, int M, int K, bs_stream_t stream) {
+  BS_CHECK(x && q && scale, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && M <= 65535 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(x, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);
+  dim3 grid((K / 8 + kThreads - 1) / kThreads, M);
+  k_group_quant<<<grid, kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(x), static_cast<uint2*>(q), scale, K);
+  return bs_launch_status();
+}
+
+BS_API int quant_fp8_block128(const void* w, void* q, float* scale, int N, int K, bs_stream_t stream) {
+  BS_CHECK(w && q && scale, BS_ERR_NULL);
+  BS_CHECK(N >= 128 && N % 128 == 0 && N / 128 <= 65535 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(w, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);
+  dim3 grid(K / 128, N / 128);
+  k_block_quant<<<grid, kThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(w), static_cast<uint2*>(q), scale, K);
+  return bs_launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/bsgemm.h declares, and rejects bad arguments on the host
+before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsgemm.h")
+LIB = os.path.join(ROOT, "block_scaled_precision_04_amd", "libbsgemm.so")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"BS_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def blib():
+    if not os.path.exists(LIB):
+        from block_scaled_precision_04_amd import build
+        build.build()
+    from block_scaled_precision_04_amd import _binding
+    return _binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    syms = set(declared_symbols())
+    for name in ("bsgemm_fp8_block", "bsgemm_w4a8_mxfp4", "gemm_bf16_skinny", "add_rms_quant_fp8",
+                 "bs_prelayout_fp8_block", "bs_prelayout_mxfp4", "bs_unprelayout_fp8_block",
+                 "bs_unprelayout_mxfp4", "bs_workspace_bytes"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(blib):
+    from block_scaled_precision_04_amd import _binding
+    for name in declared_symbols():
+        assert hasattr(blib, name), name
+        assert name in _binding.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings_and_version(blib):
+    assert blib.bs_status_string(0) == b"ok"
+    assert blib.bs_status_string(-2) == b"unsupported shape"
+    assert blib.bs_version() >= 100
+
+
+def test_sizes(blib):
+    assert blib.bs_prelayout_fp8_block_bytes(256, 512) == 256 * 512
+    assert blib.bs_prelayout_fp8_block_bytes(250, 512) == 0
+    assert blib.bs_prelayout_fp8_block_bytes(256, 500) == 0
+    # MXFP4: codes N*K/2, then 256-aligned scale section of (N/16)*ceil(KS/4)*256 bytes
+    N, K = 48, 640
+    codes = N * K // 2
+    off = (codes + 255) // 256 * 256
+    assert blib.bs_prelayout_mxfp4_bytes(N, K) == off + (N // 16) * ((K // 128 + 3) // 4) * 256
+    assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
+    assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0
+    assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails validation
+
+
+def test_gemm_argument_validation(blib):
+    from block_scaled_precision_04_amd._binding import WDesc, BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, BS_LAYOUT_MXFP4
+    d = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 512, 256 * 512, 0, 0, 256 * 512)
+    ok = dict(a=FAKE, lda=512, asp=FAKE, asm=4, asg=1, w=FAKE, ws_=FAKE, c=FAKE, ldc=256)
+
+    def fp8(M=8, N=256, K=512, desc=d, **kw):
+        p = dict(ok, **kw)
+        return blib.bsgemm_fp8_block(p["a"], p["lda"], p["asp"], p["asm"], p["asg"], ctypes.byref(desc), p["w"],
+                                     p["ws_"], p["c"], p["ldc"], M, N, K, None, 0, None)
+    assert fp8(a=None) == -1
+    assert fp8(N=200) == -2
+    assert fp8(K=500) == -2
+    assert fp8(M=0) == -2
+    assert fp8(N=384) == -4                        # descriptor says N=256
+    bad = WDesc(0, BS_LAYOUT_FP8_BLOCK, 256, 512, 0, 0, 0, 0)
+    assert fp8(desc=bad) == -4
+    assert fp8(lda=500) == -3
+    assert fp8(a=ctypes.c_void_p(0x10008)) == -3
+    assert fp8(asm=-1) == -7
+    mx = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 256 * 256, 65536, 4096, 65536 + 4096)
+    assert fp8(desc=mx) == -4                      # right shape, wrong layout
+
+    def w4(M=8, N=256, K=512, desc=mx, w=FAKE):
+        return blib.bsgemm_w4a8_mxfp4(FAKE, 512, FAKE, ctypes.byref(desc), w, FAKE, 256, M, N, K, None, 0, None)
+    assert w4(N=250) == -2
+    assert w4(desc=d) == -4
+    assert w4(w=ctypes.c_void_p(0x10010)) == -3   # the pre-laid-out weight must be 256-byte aligned
+
+
+def test_skinny_and_producer_validation(blib):
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 65, 96, 5120, None, 0, None) == -2
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5000, None, 0, None) == -2
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, None, 0, None) == -5   # K split needs a workspace
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, FAKE, 16, None) == -5
+    assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5121, None) == -2
+    assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 65536, None) == -2
+    assert blib.add_rms_quant_fp8(None, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5120, None) == -1
+    assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, 8, 5120, None) == -7
+    assert blib.quant_fp8_group128(FAKE, FAKE, FAKE, 8, 5000, None) == -2
+    assert blib.quant_fp8_block128(FAKE, FAKE, FAKE, 100, 512, None) == -2
+
+
+def test_prelayout_validation(blib):
+    from block_scaled_precision_04_amd._binding import WDesc
+    d = WDesc()
+    assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 1 << 20, 250, 512, ctypes.byref(d), None) == -2
+    assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 100, 256, 512, ctypes.byref(d), None) == -7   # out too small
+    assert blib.bs_prelayout_mxfp4(FAKE, FAKE, FAKE, 1 << 20, 32, 100, ctypes.byref(d), None) == -2
+    assert blib.bs_unprelayout_fp8_block(ctypes.byref(d), FAKE, FAKE, None) == -4             # empty descriptor

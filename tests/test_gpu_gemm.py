@@ -1,0 +1,155 @@
+"""GPU parity of the three GEMMs against the oracle (through the C ABI), at
+the workloads' own sizes (full or sampled) and at ragged / edge shapes."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_04_amd as bs
+from block_scaled_precision_04_amd import synth
+from oracle import gemm, checks
+from tests.gpu_util import (dev_u8, dev_bf16, dev_f32, host_bits16, fp8_block_inputs, w4a8_inputs,
+                            sample_grid)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ block-FP8
+def _fp8_run(aq, asc, wq, wsc, col_major_scale=False):
+    pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+    a_s = dev_f32(asc)
+    if col_major_scale:       # same values, stored [K/128, M] and read through strides
+        a_s = dev_f32(np.ascontiguousarray(asc.T)).t()
+    c = bs.bsgemm_fp8_block(dev_u8(aq), a_s, desc, pre, dev_f32(wsc))
+    torch.cuda.synchronize()
+    return host_bits16(c)
+
+
+@pytest.mark.parametrize("case", range(len(synth.WORKLOADS[2][1])))
+def test_fp8_block_decode_workload(case):
+    M, N, K = synth.WORKLOADS[2][1][case]
+    aq, asc, wq, wsc = fp8_block_inputs(2, case, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(got, ce, asum, f"fp8 block M={M} N={N} K={K}")
+
+
+def test_fp8_block_small_workload():
+    M, N, K = synth.WORKLOADS[0][1][0]
+    aq, asc, wq, wsc = fp8_block_inputs(0, 0, M, N, K)
+    got = _fp8_run(aq, asc, wq, wsc, col_major_scale=True)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(got, ce, asum, "fp8 block small")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 384), (65, 384, 640), (100, 128, 1024),
+                                   (64, 1280, 2048), (3, 5120, 17408)])
+def test_fp8_block_edges(M, N, K):
+    aq, asc, wq, wsc = fp8_block_inputs(9, M + N, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(got, ce, asum, f"fp8 block edge M={M} N={N} K={K}")
+
+
+# ------------------------------------------------------------------ MXFP4 W4A8
+def _w4_run(aq, asc, wp, e, out=None):
+    pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
+    c = bs.bsgemm_w4a8_mxfp4(dev_u8(aq), dev_f32(asc), desc, pre, out=out)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 17408, 5120), (1, 16, 128), (33, 48, 384), (64, 176, 640),
+                                   (13, 2048, 17408), (65, 48, 384), (129, 176, 640), (200, 1024, 1024),
+                                   (256, 1280, 5120), (300, 48, 17408)])
+def test_w4a8_full_oracle(M, N, K):
+    aq, asc, wp, e = w4a8_inputs(8, M + N + K, M, N, K)
+    got = host_bits16(_w4_run(aq, asc, wp, e))
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(got, ce, asum, f"w4a8 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("case", range(len(synth.WORKLOADS[3][1])))
+def test_w4a8_prefill_workload_sampled(case):
+    M, N, K = synth.WORKLOADS[3][1][case]
+    aq, asc, wp, e = w4a8_inputs(3, case, M, N, K)
+    got = host_bits16(_w4_run(aq, asc, wp, e))
+    rows, cols = sample_grid(M, N, 20, 40, seed=case)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 prefill M={M} N={N} K={K}")
+
+
+def test_w4a8_fused_chain_consumer_on_gpu_producer_output():
+    """The fused chain: the GPU producer's own (q, scale) feeds the GPU GEMM;
+    the oracle GEMM is evaluated on those same bytes, isolating GEMM error."""
+    K, N = 5120, 17408
+    wp, e = synth.mxfp4_weight_raw(4, 0, N, K)
+    pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
+    for case, M in ((0, 8), (1, 4096)):
+        y, r, w = synth.producer_raw(case, M, K)
+        q, s, _ = bs.add_rms_quant_fp8(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
+        c = bs.bsgemm_w4a8_mxfp4(q, s, desc, pre)
+        torch.cuda.synchronize()
+        qh, sh, ch = q.cpu().numpy(), s.cpu().numpy(), host_bits16(c)
+        if M <= 8:
+            _, ce, asum = gemm.w4a8_mxfp4_gemm(qh, sh, wp, e)
+            checks.assert_gemm_close(ch, ce, asum, "chain decode")
+        else:
+            rows, cols = sample_grid(M, N, 16, 32, seed=77)
+            _, ce, asum = gemm.w4a8_mxfp4_gemm_at(qh, sh, wp, e, rows, cols)
+            checks.assert_gemm_close(ch[rows, cols], ce, asum, "chain prefill")
+
+
+def test_w4a8_no_out_of_bounds_writes_and_ldc():
+    M, N, K = 150, 176, 640
+    aq, asc, wp, e = w4a8_inputs(8, 1, M, N, K)
+    big = torch.full((M + 2, N + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[1:M + 1, 8:8 + N]
+    _w4_run(aq, asc, wp, e, out=view)
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[1:M + 1, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 strided out")
+
+
+def test_determinism():
+    M, N, K = 256, 1280, 5120
+    aq, asc, wp, e = w4a8_inputs(8, 2, M, N, K)
+    a1 = host_bits16(_w4_run(aq, asc, wp, e))
+    a2 = host_bits16(_w4_run(aq, asc, wp, e))
+    assert np.array_equal(a1, a2)
+    aq, asc, wq, wsc = fp8_block_inputs(9, 3, 8, 5120, 5120)
+    assert np.array_equal(_fp8_run(aq, asc, wq, wsc), _fp8_run(aq, asc, wq, wsc))
+
+
+# ------------------------------------------------------------------ skinny bf16
+def _skinny_run(x, w):
+    M, K = x.shape
+    N = w.shape[0]
+    ws = bs.alloc_workspace(bs.BS_OP_BF16_SKINNY, M, N, K)
+    c = bs.gemm_bf16_skinny(dev_bf16(x), dev_bf16(w), ws=ws)
+    c2 = bs.gemm_bf16_skinny(dev_bf16(x), dev_bf16(w), ws=ws)     # workspace reused: counters self-reset
+    torch.cuda.synchronize()
+    h1, h2 = host_bits16(c), host_bits16(c2)
+    assert np.array_equal(h1, h2)
+    return h1
+
+
+@pytest.mark.parametrize("case", range(len(synth.WORKLOADS[1][1])))
+def test_skinny_workload(case):
+    M, N, K = synth.WORKLOADS[1][1][case]
+    x, w = synth.skinny_raw(case, M, N, K)
+    got = _skinny_run(x, w)
+    _, ce, asum = gemm.bf16_gemm(x, w)
+    checks.assert_gemm_close(got, ce, asum, f"skinny M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 32, 384), (33, 48, 640), (64, 16, 128), (5, 1280, 5120)])
+def test_skinny_edges(M, N, K):
+    g = synth.rng(M * 1000 + N + K)
+    x = synth.bf16_normal(g, (M, K), 1.0)
+    w = synth.bf16_normal(g, (N, K), 0.02)
+    got = _skinny_run(x, w)
+    _, ce, asum = gemm.bf16_gemm(x, w)
+    checks.assert_gemm_close(got, ce, asum, f"skinny edge M={M} N={N} K={K}")
