@@ -79,6 +79,8 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
            BS_ERR_ALIGN);
+  // the tiled kernel addresses the activation with 32-bit offsets
+  BS_CHECK(static_cast<uint64_t>(M) * static_cast<uint64_t>(lda) < (1ull << 32), BS_ERR_SHAPE);
   const uint8_t* w = static_cast<const uint8_t*>(w_pre);
   const uint32_t* wsc = reinterpret_cast<const uint32_t*>(w + wd->scales_offset);
   hipStream_t st = static_cast<hipStream_t>(stream);

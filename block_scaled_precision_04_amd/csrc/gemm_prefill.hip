@@ -7,110 +7,153 @@
 // MFMA V_MFMA_SCALE_F32_32X32X64_F8F6F4 takes the e2m1 weight and the e4m3
 // activation directly and applies the MX e8m0 block scale (one per 32 K) in
 // hardware, so the exact dequantised product of the page's _exact_ref is
-// accumulated in fp32 with no software decode at all.
+// accumulated in fp32 with no software decode at all.  The mixed fp4 x fp8
+// instruction issues at the FP8 rate.
 //
 // Tiling: a workgroup computes a BM x BN output tile with WM x WN waves; each
-// wave owns (BM/WM) x (BN/WN) as 32x32 MFMA sub-tiles with fp32 accumulators.
-// K advances in 128-wide steps.  Each step's activation tile (BM x 128 bytes,
-// row pitch padded to avoid LDS bank conflicts) and weight tile (BN/16
-// fragment-order 1 KiB blocks, copied as they are) are staged through LDS,
-// double buffered: the global loads of step k+1 are in flight while step k
-// is computed.  The e8m0 scales are read straight from the pre-laid-out
-// scale section (one dword per lane per 4 steps).  The per-token activation
-// scale multiplies the accumulator in the epilogue, then bf16 RNE and store.
-// The first MFMA operand is the weight (rows = n), the second the activation
-// (rows = m), so each lane stores four consecutive n of one m (8 bytes).
+// wave owns (BM/WM) x (BN/WN) as 32x32 MFMA sub-tiles with fp32 accumulators
+// (the large tiles keep them in the accumulator registers).  K advances in
+// 128-wide steps.  Each step's activation tile (BM rows x 128 bytes) and
+// weight tile (BN/16 fragment-order 1 KiB blocks, copied as they are) are
+// moved global -> LDS by the direct-to-LDS 16-byte load (no register
+// staging), double buffered: the loads of step k+1 are in flight while step
+// k is computed.  Activation rows are stored without padding; their eight
+// 16-byte chunks are XOR-swizzled by the row index so that the fragment reads
+// (32 rows, same chunk) spread over the LDS banks.  The e8m0 scales are read
+// straight from the pre-laid-out scale section (one dword per lane per four
+// steps).  The per-token activation scale multiplies the accumulator in the
+// epilogue, then bf16 RNE and store.  The first MFMA operand is the weight
+// (rows = n), the second the activation (rows = m), so each lane stores four
+// consecutive n of one m (8 bytes).
+//
+// Workgroup -> tile order: gfx950 hands workgroup b to XCD b % 8, and each
+// XCD has its own L2.  The tile sequence is cut into eight contiguous chunks,
+// one per XCD, and inside a chunk tiles follow a grouped raster (GROUP_M
+// m-tiles sweep the n-tiles together), so the workgroups resident on one XCD
+// at any moment share a few activation and weight tiles in that XCD's L2.
 #include "common.h"
 
 namespace {
 
-constexpr int kApitch = 144;  // bytes per staged activation row (128 + 16 pad)
+constexpr int kXcds = 8;
+
+BS_INLINE int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 template <int BM, int BN, int WM, int WN>
 struct PrefillCfg {
   static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaves = WM * WN;
   static constexpr int kTM = BM / WM / 32;  // 32-row sub-tiles per wave along m
   static constexpr int kTN = BN / WN / 32;  // along n
-  static constexpr int kAChunks = BM * 8;   // 16-byte chunks of one activation tile
-  static constexpr int kBChunks = BN * 4;   // of one weight tile (BN/16 x 64 lanes)
-  static constexpr int kAPer = kAChunks / kThreads;
-  static constexpr int kBPer = kBChunks / kThreads;
-  static constexpr int kAStage = BM * kApitch;
-  static constexpr int kBStage = BN * 64;
-  static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0, "tile / thread mismatch");
+  static constexpr int kAStage = BM * 128;  // bytes of one staged activation tile
+  static constexpr int kBStage = BN * 64;   // bytes of one staged weight tile
+  static constexpr int kSStage = BN * 16;   // e8m0 dwords of the tile's n-tiles for four K steps
+  static constexpr int kStage = kAStage + kBStage + kSStage;
+  static constexpr int kAIters = kAStage / (kThreads * 16);
+  static constexpr int kBIters = kBStage / (kThreads * 16);
+  static constexpr int kSIters = (kSStage + kThreads * 16 - 1) / (kThreads * 16);
+  // direct-to-LDS loads per stage issued by every wave (waves past the scale
+  // region skip its load, so this is the count the slowest-issuing wave has)
+  static constexpr int kDmaMin = kAIters + kBIters + kSStage / (kThreads * 16);
+  static constexpr int kDmaAll = kAIters + kBIters + kSIters;
+  static_assert(kAStage % (kThreads * 16) == 0 && kBStage % (kThreads * 16) == 0, "tile / thread mismatch");
+  static_assert(kSStage % 1024 == 0, "scale stage must be whole waves");
   static_assert(kTM >= 1 && kTN >= 1, "wave tile too small");
 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void k_w4a8_prefill(
-    const uint8_t* __restrict__ a, int64_t lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
-    const uint32_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m) {
+// Direct-to-LDS 16-byte load: lane i's 16 bytes from sbase + voff land at LDS
+// byte address lds_addr + 16*i.  Issued from inline assembly so that the
+// compiler does not serialise it against the LDS reads of other stages; the
+// kernel waits for these loads itself (vmcnt) before the barrier that
+// publishes a stage.
+BS_INLINE void dma16(uint32_t lds_addr, const void* sbase, uint32_t voff) {
+  // one wait state between the M0 write and the LDS-DMA that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads outstanding
+template <int N>
+BS_INLINE void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile t of the grouped raster: group_m m-tiles sweep the n-tiles together.
+BS_INLINE void tile_mn(int t, int m_tiles, int n_tiles, int group_m, int& mt, int& nt) {
+  const int per_group = group_m * n_tiles;
+  const int grp = t / per_group;
+  const int first_m = grp * group_m;
+  const int gsize = min(m_tiles - first_m, group_m);
+  const int loc = t - grp * per_group;
+  mt = first_m + loc % gsize;
+  nt = loc / gsize;
+}
+
+// One workgroup per output tile.  Workgroup b runs on XCD b % 8; the tile
+// sequence is cut into eight contiguous chunks, one per XCD, so the
+// workgroups resident on one XCD at any moment are neighbours in the grouped
+// raster and share activation / weight tiles in that XCD's L2.
+template <int BM, int BN, int WM, int WN, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
+    const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
+    const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m) {
   using C = PrefillCfg<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][C::kAStage];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][C::kBStage];
+  constexpr int STAGES = 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int NT = N >> 4;
   const int KQ = (KS + 3) >> 2;
-
-  // grouped raster: group_m m-tiles share one sweep over the n-tiles
-  const int n_tiles = (N + BN - 1) / BN;
-  const int m_tiles = (M + BM - 1) / BM;
-  const int bid = blockIdx.x;
-  const int per_group = group_m * n_tiles;
-  const int grp = bid / per_group;
-  const int first_m = grp * group_m;
-  const int gsize = min(m_tiles - first_m, group_m);
-  const int mt = first_m + (bid % per_group) % gsize;
-  const int ntile = (bid % per_group) / gsize;
+  const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int T = m_tiles * n_tiles;
+  const int x = blockIdx.x % kXcds, jj = blockIdx.x / kXcds;
+  const int cq = T / kXcds, cr = T % kXcds;
+  int mt, ntile;
+  tile_mn(x * cq + min(x, cr) + jj, m_tiles, n_tiles, group_m, mt, ntile);
   const int m0 = mt * BM, n0 = ntile * BN;
   const int nt0 = n0 >> 4;
 
-  // ---- global -> register prefetch of one K step
-  uint4 ra[C::kAPer], rb[C::kBPer];
-  auto gload = [&](int ks) {
+  // ---- per-lane 32-bit source offsets of the direct-to-LDS loads.  A load
+  // instruction writes lane i's 16 bytes at (uniform LDS base) + 16*i, so each
+  // lane fetches the chunk that belongs at its LDS position.  Rows past M and
+  // n-tiles past N fetch the last valid row / tile (finite data, never stored).
+  uint32_t aoff[C::kAIters];
 #pragma unroll
-    for (int i = 0; i < C::kAPer; ++i) {
-      const int ch = i * C::kThreads + tid;
-      const int row = ch >> 3, col = ch & 7;
-      const int m = m0 + row;
-      ra[i] = m < M ? *reinterpret_cast<const uint4*>(a + m * lda + ks * 128 + col * 16) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < C::kAIters; ++i) {
+    const int p = (i * C::kWaves + wave) * 64 + l;  // 16-byte position in the activation stage
+    const int row = p >> 3, slot = p & 7;
+    aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1) * lda + 16 * swz(row, slot));
+  }
+  uint32_t boff_g[C::kBIters];
 #pragma unroll
-    for (int i = 0; i < C::kBPer; ++i) {
-      const int ch = i * C::kThreads + tid;
-      const int ntl = ch >> 6, ln = ch & 63;
-      const int nt = nt0 + ntl;
-      rb[i] = nt < NT ? *reinterpret_cast<const uint4*>(w + (static_cast<size_t>(nt) * KS + ks) * 1024 + ln * 16)
-                      : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int i = 0; i < C::kBIters; ++i) {
+    const int nt = min(nt0 + i * C::kWaves + wave, NT - 1);
+    boff_g[i] = static_cast<uint32_t>(nt * KS * 1024 + l * 16);
+  }
+  uint32_t soff_g[C::kSIters];
 #pragma unroll
-    for (int i = 0; i < C::kAPer; ++i) {
-      const int ch = i * C::kThreads + tid;
-      *reinterpret_cast<uint4*>(&lds_a[buf][(ch >> 3) * kApitch + (ch & 7) * 16]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::kBPer; ++i) {
-      const int ch = i * C::kThreads + tid;
-      *reinterpret_cast<uint4*>(&lds_b[buf][ch * 16]) = rb[i];
-    }
-  };
-  // ---- per-lane e8m0 scale dwords for one K step: [p][hh]
-  uint32_t sd[C::kTN][2];
-  auto sload = [&](int ks) {
-#pragma unroll
-    for (int p = 0; p < C::kTN; ++p) {
-      const int n = n0 + wn * (BN / WN) + 32 * p + (l & 31);
-      const int nt = n >> 4;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int lanep = (n & 15) + 16 * (2 * hh + (l >> 5));
-        sd[p][hh] = nt < NT ? wsc[(static_cast<size_t>(nt) * KQ + (ks >> 2)) * 64 + lanep] : 0x7F7F7F7Fu;
-      }
+  for (int i = 0; i < C::kSIters; ++i) {
+    const int p = (i * C::kWaves + wave) * 64 + l;
+    const int nt = min(nt0 + (p >> 4), NT - 1);
+    soff_g[i] = static_cast<uint32_t>(nt * KQ * 256 + (p & 15) * 16);
+  }
+  // the i-th direct-to-LDS load of step ks (i < kDmaAll) into buffer buf
+  auto dma_one = [&](int i, int ks, int buf) {
+    const uint32_t base = lds0 + buf * C::kStage;
+    if (i < C::kAIters) {
+      dma16(base + (i * C::kWaves + wave) * 1024, a + ks * 128, aoff[i]);
+    } else if (i < C::kAIters + C::kBIters) {
+      const int j = i - C::kAIters;
+      dma16(base + C::kAStage + (j * C::kWaves + wave) * 1024, w + static_cast<size_t>(ks) * 1024, boff_g[j]);
+    } else {
+      const int j = i - C::kAIters - C::kBIters;
+      if (C::kSStage % (C::kThreads * 16) == 0 || (j * C::kWaves + wave) * 1024 < C::kSStage)
+        dma16(base + C::kAStage + C::kBStage + (j * C::kWaves + wave) * 1024, wsc + (ks >> 2) * 256, soff_g[j]);
     }
   };
 
@@ -120,67 +163,125 @@ __global__ __launch_bounds__(64 * WM * WN) void k_w4a8_prefill(
 #pragma unroll
     for (int q = 0; q < C::kTM; ++q) acc[p][q] = v16f{};
 
-  gload(0);
-  sstore(0);
-  sload(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < KS; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < KS;
-    if (more) gload(ks + 1);
-    uint32_t scur[C::kTN][2];
+  // fragment LDS offsets (within a stage) that do not depend on the K step
+  int boff[C::kTN][2], soff[C::kTN][2];
 #pragma unroll
-    for (int p = 0; p < C::kTN; ++p) {
-      scur[p][0] = sd[p][0] >> (8 * (ks & 3));
-      scur[p][1] = sd[p][1] >> (8 * (ks & 3));
-    }
-    if (more && ((ks + 1) & 3) == 0) sload(ks + 1);
+  for (int p = 0; p < C::kTN; ++p) {
+    const int nl = wn * (BN / WN) + 32 * p + (l & 31);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      v8i bf[C::kTN], af[C::kTM];
+      const int lanep = (nl & 15) + 16 * (2 * hh + (l >> 5));
+      boff[p][hh] = C::kAStage + (nl >> 4) * 1024 + lanep * 16;
+      soff[p][hh] = C::kAStage + C::kBStage + (nl >> 4) * 256 + lanep * 4;
+    }
+  }
+  int arow[C::kTM];
 #pragma unroll
-      for (int p = 0; p < C::kTN; ++p) {
-        const int nl = wn * (BN / WN) + 32 * p + (l & 31);
-        const int lanep = (nl & 15) + 16 * (2 * hh + (l >> 5));
-        const uint4 x = *reinterpret_cast<const uint4*>(&lds_b[buf][(nl >> 4) * 1024 + lanep * 16]);
-        bf[p] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-      }
+  for (int q = 0; q < C::kTM; ++q) arow[q] = wm * (BM / WM) + 32 * q + (l & 31);
+
+  // fragments of one half step (64 K): weight, activation, e8m0 dword per p
+  struct Frag {
+    v8i b[C::kTN];
+    v8i a[C::kTM];
+    uint32_t s[C::kTN];
+  };
+  auto lds_frags = [&](const uint8_t* st, int hh, Frag& f) {
+#pragma unroll
+    for (int p = 0; p < C::kTN; ++p) {
+      const uint4 v = *reinterpret_cast<const uint4*>(st + boff[p][hh]);
+      f.b[p] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      f.s[p] = *reinterpret_cast<const uint32_t*>(st + soff[p][hh]);
+    }
+#pragma unroll
+    for (int q = 0; q < C::kTM; ++q) {
+      // chunks 4hh + g and 4hh + 2 + g of the row (the 8-bit operand's order)
+      const int r = arow[q];
+      const int c0 = 4 * hh + (l >> 5);
+      const uint4 u = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0));
+      const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0 + 2));
+      f.a[q] = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    }
+  };
+  // MFMAs of one half step; with dks >= 0 the loads of step dks (into buffer
+  // dbuf) are issued between them (one after each MFMA), so the load unit is
+  // fed steadily and the wave never stalls on a burst of loads
+  auto mma = [&](const Frag& f, int sh, int dks, int dbuf) {
+#pragma unroll
+    for (int p = 0; p < C::kTN; ++p) {
+      const int sc = static_cast<int>(f.s[p] >> sh);
 #pragma unroll
       for (int q = 0; q < C::kTM; ++q) {
-        const int ml = wm * (BM / WM) + 32 * q + (l & 31);
-        const uint8_t* row = &lds_a[buf][ml * kApitch + 64 * hh + 16 * (l >> 5)];
-        const uint4 x = *reinterpret_cast<const uint4*>(row);
-        const uint4 y = *reinterpret_cast<const uint4*>(row + 32);
-        af[q] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[p], f.a[q], acc[p][q], 4, 0, 0, sc, 0, 127);
+        const int i = p * C::kTM + q;
+        if (i < C::kDmaAll && dks >= 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma_one(i, dks, dbuf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-#pragma unroll
-      for (int p = 0; p < C::kTN; ++p)
-#pragma unroll
-        for (int q = 0; q < C::kTM; ++q)
-          acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[p], af[q], acc[p][q], 4, 0, 0,
-                                                                      static_cast<int>(scur[p][hh]), 0, 127);
     }
-    if (more) sstore(buf ^ 1);
+    // loads left over when a half step has fewer MFMAs than loads
+#pragma unroll
+    for (int i = C::kTN * C::kTM; i < C::kDmaAll; ++i)
+      if (dks >= 0) dma_one(i, dks, dbuf);
+  };
+
+  // Pipeline: three LDS buffers (buffer of step s = s % 3), fragment register
+  // sets f0 / f1 for the two 64-K halves of a step.  Step ks:
+  //   MFMAs on f0, with the loads of step ks+2 (into the buffer step ks-1 used)
+  //   issued one per MFMA; refill f1 from LDS; MFMAs on f1; wait until this
+  //   wave's loads of step ks+1 have landed and its LDS reads are done;
+  //   barrier (publishes step ks+1, frees buffer ks for step ks+3); refill f0
+  //   with the first half of step ks+1.
+  // The loads stay two steps ahead of their use.
+#pragma unroll
+  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, min(1, KS - 1), 1);
+  wait_vm<C::kDmaMin>();
+  __syncthreads();
+  Frag f0, f1;
+  lds_frags(lds, 0, f0);
+
+  int buf = 0;
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint8_t* st = lds + buf * C::kStage;
+    const int sh = 8 * (ks & 3);
+    int pbuf = buf + 2;
+    if (pbuf >= STAGES) pbuf -= STAGES;
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0, sh, min(ks + 2, KS - 1), pbuf);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_frags(st, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1, sh, -1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<C::kDmaMin>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
+    buf = buf + 1 == STAGES ? 0 : buf + 1;
+    // (after the last step this reads a buffer whose values are never used;
+    // reading unconditionally keeps the loop body one basic block)
+    lds_frags(lds + buf * C::kStage, 0, f0);
   }
+  wait_vm<0>();
 
   // ---- epilogue: x per-token scale, bf16 RNE, 8-byte stores
 #pragma unroll
   for (int q = 0; q < C::kTM; ++q) {
-    const int m = m0 + wm * (BM / WM) + 32 * q + (l & 31);
+    const int m = m0 + arow[q];
     if (m >= M) continue;
-    const float s = as[m];
+    const float sc = as[m];
 #pragma unroll
     for (int p = 0; p < C::kTN; ++p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = n0 + wn * (BN / WN) + 32 * p + 8 * i + 4 * (l >> 5);
         if (n < N) {
-          const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * s);
-          const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * s);
-          const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * s);
-          const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * s);
+          const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
+          const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
+          const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
+          const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
           *reinterpret_cast<uint2*>(c + m * ldc + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         }
       }
@@ -188,15 +289,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k_w4a8_prefill(
   }
 }
 
+template <int BM, int BN, int WM, int WN, int OCC>
+int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint8_t* wsc, uint16_t* c,
+               int64_t ldc, int M, int N, int KS, int group_m, hipStream_t st) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  k_w4a8_prefill<BM, BN, WM, WN, OCC><<<tiles, 64 * WM * WN, 0, st>>>(a, static_cast<int>(lda), as, w, wsc, c, ldc, M,
+                                                                    N, KS, group_m);
+  return bs_launch_status();
+}
+
 }  // namespace
 
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                            uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st) {
   const int KS = K / 128;
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
-  const int n_tiles = (N + BN - 1) / BN, m_tiles = (M + BM - 1) / BM;
-  const int group_m = 8;
-  k_w4a8_prefill<BM, BN, WM, WN><<<n_tiles * m_tiles, 64 * WM * WN, 0, st>>>(a, lda, as, w, wsc, c, ldc, M, N, KS,
-                                                                            group_m);
-  return bs_launch_status();
+  const long big_tiles = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 256) return launch_cfg<256, 256, 2, 2, 1>(a, lda, as, w, reinterpret_cast<const uint8_t*>(wsc), c, ldc, M, N, KS, 4, st);
+  return launch_cfg<128, 128, 2, 2, 2>(a, lda, as, w, reinterpret_cast<const uint8_t*>(wsc), c, ldc, M, N, KS, 4, st);
 }
