@@ -226,44 +226,54 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       if (dks >= 0) dma_one(i, dks, dbuf);
   };
 
-  // Pipeline: three LDS buffers (buffer of step s = s % 3), fragment register
-  // sets f0 / f1 for the two 64-K halves of a step.  Step ks:
-  //   MFMAs on f0, with the loads of step ks+2 (into the buffer step ks-1 used)
-  //   issued one per MFMA; refill f1 from LDS; MFMAs on f1; wait until this
-  //   wave's loads of step ks+1 have landed and its LDS reads are done;
-  //   barrier (publishes step ks+1, frees buffer ks for step ks+3); refill f0
-  //   with the first half of step ks+1.
-  // The loads stay two steps ahead of their use.
+  // Pipeline: three LDS buffers (buffer of step s = s % 3) and three fragment
+  // register sets rotating over the 64-K halves.  The matrix unit queues a
+  // wave's MFMAs and reads their operand registers only when each one starts,
+  // so a register set is refilled only once the MFMAs that read it are two
+  // halves back in the queue.  Step s, with sets (X, Y, Z):
+  //   MFMAs on X (first half of s), with the loads of step s+2 (into the
+  //   buffer step s-1 used) issued one per MFMA; refill Y with the second half
+  //   of s; MFMAs on Y; wait until this wave's loads of step s+1 have landed
+  //   and its LDS reads are done; barrier (publishes step s+1, frees buffer s
+  //   for step s+3); refill Z with the first half of step s+1.
+  // The next step uses (Z, X, Y).  The loads stay two steps ahead of their use.
 #pragma unroll
   for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, 0, 0);
 #pragma unroll
   for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, min(1, KS - 1), 1);
   wait_vm<C::kDmaMin>();
   __syncthreads();
-  Frag f0, f1;
+  Frag f0, f1, f2;
   lds_frags(lds, 0, f0);
 
   int buf = 0;
-  for (int ks = 0; ks < KS; ++ks) {
+  auto step = [&](int ks, Frag& fx, Frag& fy, Frag& fz) {
     const uint8_t* st = lds + buf * C::kStage;
     const int sh = 8 * (ks & 3);
     int pbuf = buf + 2;
     if (pbuf >= STAGES) pbuf -= STAGES;
     __builtin_amdgcn_sched_barrier(0);
-    mma(f0, sh, min(ks + 2, KS - 1), pbuf);
+    mma(fx, sh, min(ks + 2, KS - 1), pbuf);
     __builtin_amdgcn_sched_barrier(0);
-    lds_frags(st, 1, f1);
+    lds_frags(st, 1, fy);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f1, sh, -1, 0);
+    mma(fy, sh, -1, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<C::kDmaMin>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
     buf = buf + 1 == STAGES ? 0 : buf + 1;
-    // (after the last step this reads a buffer whose values are never used;
-    // reading unconditionally keeps the loop body one basic block)
-    lds_frags(lds + buf * C::kStage, 0, f0);
+    // (after the last step this reads a buffer whose values are never used)
+    lds_frags(lds + buf * C::kStage, 0, fz);
+  };
+  int ks = 0;
+  for (; ks + 3 <= KS; ks += 3) {
+    step(ks, f0, f1, f2);
+    step(ks + 1, f2, f0, f1);
+    step(ks + 2, f1, f2, f0);
   }
+  if (ks < KS) step(ks++, f0, f1, f2);
+  if (ks < KS) step(ks++, f2, f0, f1);
   wait_vm<0>();
 
   // ---- epilogue: x per-token scale, bf16 RNE, 8-byte stores
