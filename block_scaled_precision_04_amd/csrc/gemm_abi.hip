@@ -5,9 +5,10 @@
 
 int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, int64_t asm_, int64_t asg,
                                const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
-                               hipStream_t st);
+                               void* work, hipStream_t st);
 int bs_launch_w4a8_decode(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                          uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st);
+                          uint16_t* c, int64_t ldc, int M, int N, int K, void* work, hipStream_t st);
+size_t bs_decode_workspace(int M, int N, int K, bool mx);
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                            uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st);
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
@@ -17,6 +18,15 @@ size_t bs_skinny_workspace(int M, int N, int K);
 namespace {
 constexpr int kW4A8DecodeMaxM = 64;  // above this the compute-bound tiled kernel runs
 constexpr int kSkinnyMaxM = 64;
+constexpr int kFp8MaxM = 1 << 20;
+
+// A split-K launch needs a workspace of at least `need` bytes, 256-aligned.
+int check_workspace(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return BS_OK;
+  if (ws == nullptr || ws_bytes < need) return BS_ERR_WORKSPACE;
+  if (!bs_aligned(ws, 256)) return BS_ERR_ALIGN;
+  return BS_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -42,35 +52,41 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K) {
     if (M < 1 || M > kSkinnyMaxM || N < 16 || N % 16 || K < 128 || K % 128) return 0;
     return bs_skinny_workspace(M, N, K);
   }
-  return 0;  // the block-FP8 and W4A8 kernels reduce split-K inside a workgroup
+  if (op == BS_OP_FP8_BLOCK) {
+    if (M < 1 || M > kFp8MaxM || N < 128 || N % 128 || K < 128 || K % 128) return 0;
+    return bs_decode_workspace(M, N, K, false);
+  }
+  if (op == BS_OP_W4A8_MXFP4) {
+    if (M < 1 || M > kW4A8DecodeMaxM || N < 16 || N % 16 || K < 128 || K % 128) return 0;
+    return bs_decode_workspace(M, N, K, true);
+  }
+  return 0;
 }
 
 BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, int64_t as_stride_m,
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre, const float* w_scale,
                             void* c, int64_t ldc, int M, int N, int K, void* ws, size_t ws_bytes,
                             bs_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   BS_CHECK(a && a_scale && wd && w_pre && w_scale && c, BS_ERR_NULL);
-  BS_CHECK(M >= 1 && M <= (1 << 20) && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
-  BS_CHECK(N / 16 <= 0x7FFFFFFF && (M + 15) / 16 <= 65535, BS_ERR_SHAPE);
+  BS_CHECK(M >= 1 && M <= kFp8MaxM && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_FP8_BLOCK && wd->N == N && wd->K == K,
            BS_ERR_LAYOUT);
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
+  BS_CHECK(lda < (1 << 25), BS_ERR_SHAPE);  // activation rows are addressed with 32-bit offsets
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 16) && bs_aligned(c, 16) && bs_aligned(a_scale, 4) &&
                bs_aligned(w_scale, 4),
            BS_ERR_ALIGN);
   BS_CHECK(as_stride_m >= 0 && as_stride_g >= 0, BS_ERR_ARG);
+  const int wst = check_workspace(bs_decode_workspace(M, N, K, false), ws, ws_bytes);
+  if (wst != BS_OK) return wst;
   return bs_launch_fp8_block_decode(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,
                                     static_cast<const uint8_t*>(w_pre), w_scale, static_cast<uint16_t*>(c), ldc,
-                                    M, N, K, static_cast<hipStream_t>(stream));
+                                    M, N, K, ws, static_cast<hipStream_t>(stream));
 }
 
 BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, const bs_wdesc* wd,
                              const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
                              size_t ws_bytes, bs_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   BS_CHECK(a && a_scale && wd && w_pre && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= (1 << 22) && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_MXFP4 && wd->N == N && wd->K == K &&
@@ -79,14 +95,17 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
            BS_ERR_ALIGN);
-  // the tiled kernel addresses the activation with 32-bit offsets
-  BS_CHECK(static_cast<uint64_t>(M) * static_cast<uint64_t>(lda) < (1ull << 32), BS_ERR_SHAPE);
+  // both kernels address the activation with 32-bit offsets
+  BS_CHECK(static_cast<uint64_t>(M) * static_cast<uint64_t>(lda) < (1ull << 32) && lda < (1 << 25), BS_ERR_SHAPE);
   const uint8_t* w = static_cast<const uint8_t*>(w_pre);
   const uint32_t* wsc = reinterpret_cast<const uint32_t*>(w + wd->scales_offset);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (M <= kW4A8DecodeMaxM)
+  if (M <= kW4A8DecodeMaxM) {
+    const int wst = check_workspace(bs_decode_workspace(M, N, K, true), ws, ws_bytes);
+    if (wst != BS_OK) return wst;
     return bs_launch_w4a8_decode(static_cast<const uint8_t*>(a), lda, a_scale, w, wsc, static_cast<uint16_t*>(c),
-                                 ldc, M, N, K, st);
+                                 ldc, M, N, K, ws, st);
+  }
   return bs_launch_w4a8_prefill(static_cast<const uint8_t*>(a), lda, a_scale, w, wsc, static_cast<uint16_t*>(c),
                                 ldc, M, N, K, st);
 }
@@ -96,11 +115,8 @@ BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N,
   BS_CHECK(x && w && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= kSkinnyMaxM && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(w, 16) && bs_aligned(c, 4), BS_ERR_ALIGN);
-  const size_t need = bs_skinny_workspace(M, N, K);
-  if (need > 0) {
-    BS_CHECK(ws != nullptr && ws_bytes >= need, BS_ERR_WORKSPACE);
-    BS_CHECK(bs_aligned(ws, 256), BS_ERR_ALIGN);
-  }
+  const int wst = check_workspace(bs_skinny_workspace(M, N, K), ws, ws_bytes);
+  if (wst != BS_OK) return wst;
   return bs_launch_skinny(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                           static_cast<uint16_t*>(c), M, N, K, ws, static_cast<hipStream_t>(stream));
 }

@@ -4,18 +4,30 @@
 // one scale per 128x128 block, e4m3 activations with one scale per token per
 // 128-wide K group) and MXFP4 W4A8 at small M (radiance_mxfp4.py page: the
 // decode band, the fragment-order weight that makes a wave's weight read
-// contiguous, and split-K for shapes with too little N to fill the GPU).
+// contiguous, and split-K for shapes with too little N to fill the GPU; the
+// decode split-K scratch whose last-arriving block reduces and resets it).
 //
 // At M <= 64 the weight bytes dominate: the arithmetic intensity is far below
-// the MFMA ridge, so the kernel is built to keep HBM busy:
+// the MFMA ridge, so the kernel is built to keep HBM busy and to spend as few
+// memory instructions as possible on anything but the weight:
 //   * the weight was pre-laid-out in fragment order, so one (16-row tile,
 //     128-K step) is one contiguous 2 KiB (fp8) / 1 KiB (fp4) block and each
 //     lane issues 16-byte loads;
-//   * a workgroup owns one 16-column tile of the output and splits K across
-//     its SK waves; each wave first issues the loads of S steps at once, then
-//     consumes them, so many KiB per CU are in flight;
-//   * partial sums are reduced across the waves through LDS in a fixed order
-//     (deterministic), then rounded once to bf16.
+//   * a wave owns T 16-column tiles over the R K steps of its split and
+//     issues all of its weight loads at once, straight into registers;
+//   * the activation slice of a split (R steps x up to 16*MB rows) is copied
+//     once per workgroup into LDS by direct-to-LDS loads in which every lane
+//     fetches useful bytes, and the TW*T tiles of the workgroup read their
+//     MFMA fragments from there -- per-wave activation loads (half of whose
+//     lanes repeat rows when M < 16) cost as many memory instructions as the
+//     weight itself;
+//   * when K has more than one split, the last workgroup of a tile group to
+//     finish (atomic counter) adds the S fp32 partials in split order, then
+//     resets its counter -- deterministic, and the workspace stays ready;
+//   * one rounding to bf16 at the end.
+// Every load is unconditional: rows past M and steps past K re-read valid
+// bytes and are masked afterwards, because loads inside data-dependent
+// branches make the compiler wait for all outstanding loads at each branch.
 // The MFMA puts the weight tile in the first operand (rows = n) and the
 // activations in the second (rows = m), so D[n][m] and each lane holds four
 // consecutive n of one m.
@@ -24,33 +36,26 @@
 // its result (fresh accumulator) is scaled by a_scale[m,g] * w_scale[n/128,g]
 // and added into an fp32 accumulator.  MXFP4: the scaled MFMA applies the e8m0
 // weight scales in hardware (activation scale byte 127 = 1.0) and accumulates;
-// the per-token activation scale multiplies the sum at the end.
+// the per-token activation scale multiplies the sum at the end.  The fp8 x fp8
+// fragments hold K offsets 32*(l/16) .. +32 on both sides; an 8-bit operand
+// paired with a 4-bit one holds 16g.. and 64+16g.. (gfx950), while the 4-bit
+// operand holds 32g..32g+31, so the activation fragment follows the hardware's
+// 8-bit order and real K lines up with the weight.
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
 
-// ---- fragment loads --------------------------------------------------------
-// fp8 x fp8 MFMA: both operands hold, in lane l, 32 bytes for K offsets
-// 32*(l/16) .. +32 of a 128-K step (the same order on both sides, so the
-// pairing is exact).
-BS_INLINE v8i load_a_fp8_contig(const uint8_t* a, int64_t lda, int m, int M, int k) {
-  if (m >= M) return v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  const uint4* p = reinterpret_cast<const uint4*>(a + m * lda + k);
-  uint4 x = p[0], y = p[1];
+BS_INLINE v8i pack8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
-// fp8 operand paired with an fp4 operand: the 8-bit operand's bytes 0..15 of
-// lane group g are K offsets 16g.., bytes 16..31 are 64+16g.. (gfx950), while
-// the 4-bit operand holds 32g..32g+31; so the activation loads follow the
-// hardware's 8-bit order and real K lines up with the weight.
-BS_INLINE v8i load_a_fp8_split(const uint8_t* a, int64_t lda, int m, int M, int k0, int g) {
-  if (m >= M) return v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  const uint8_t* row = a + m * lda + k0;
-  uint4 x = *reinterpret_cast<const uint4*>(row + 16 * g);
-  uint4 y = *reinterpret_cast<const uint4*>(row + 64 + 16 * g);
-  return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+BS_INLINE v8i keep_if(v8i v, bool keep) {
+  v8i z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = keep ? v[i] : 0;
+  return z;
 }
-
 BS_INLINE v4f mfma_fp8(v8i w, v8i a, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, c, 0, 0, 0, 127, 0, 127);
 }
@@ -58,192 +63,384 @@ BS_INLINE v4f mfma_fp4w_fp8a(v8i w, v8i a, v4f c, int wscale) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, c, 4, 0, 0, wscale, 0, 127);
 }
 
-// ---- cross-wave reduction and store -----------------------------------------
-// red: [SK][MB*4][64] floats.  Every thread of the workgroup sums some outputs
-// over the waves in wave order, then stores bf16.
-template <int MB>
-BS_INLINE void reduce_store(const v4f (&acc)[MB], float* red, int nwaves, uint16_t* c, int64_t ldc, int M,
-                            int n0, int m0, const float* a_scale_tok) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * MB * 4 + mb * 4 + r) * 64 + l] = acc[mb][r];
-  __syncthreads();
-  for (int o = threadIdx.x; o < MB * 4 * 64; o += blockDim.x) {
-    float s = 0.0f;
-    for (int w = 0; w < nwaves; ++w) s += red[w * MB * 4 * 64 + o];
-    const int lane = o & 63, r = (o >> 6) & 3, mb = o >> 8;
-    const int m = m0 + 16 * mb + (lane & 15);
-    const int n = n0 + 4 * (lane >> 4) + r;
-    if (m < M) {
-      if (a_scale_tok) s *= a_scale_tok[m];
-      c[m * ldc + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
-    }
-  }
-}
-
-// ---- block-FP8 --------------------------------------------------------------
-// grid (N/16, ceil(M/(16*MB))), block 64*SK threads.  Wave w handles the K
-// steps [w*per, min((w+1)*per, KS)) in chunks of S.
-template <int MB, int S>
-__global__ __launch_bounds__(512) void k_fp8_block_decode(
-    const uint8_t* __restrict__ a, int64_t lda, const float* __restrict__ as, int64_t asm_, int64_t asg,
-    const uint8_t* __restrict__ w, const float* __restrict__ ws, uint16_t* __restrict__ c, int64_t ldc, int M,
-    int KS, int per) {
-  extern __shared__ float red[];
-  const int nt = blockIdx.x;
-  const int m0 = blockIdx.y * 16 * MB;
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int nwaves = blockDim.x >> 6;
-  const int g = l >> 4;
-  const uint8_t* wt = w + static_cast<size_t>(nt) * KS * 2048 + l * 16;
-  const float* wsc = ws + static_cast<size_t>(nt >> 3) * KS;  // 8 16-row tiles per 128-row block
-  v4f acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0, 0, 0, 0};
-  const int kbeg = wave * per;
-  const int kend = min(kbeg + per, KS);
-  for (int base = kbeg; base < kend; base += S) {
-    v8i wf[S];
-    v8i af[S][MB];
-    float sa[S][MB];
-    float sw[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int ks = base + s;
-      if (ks < kend) {
-        const uint4 x = *reinterpret_cast<const uint4*>(wt + static_cast<size_t>(ks) * 2048);
-        const uint4 y = *reinterpret_cast<const uint4*>(wt + static_cast<size_t>(ks) * 2048 + 1024);
-        wf[s] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        sw[s] = wsc[ks];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = m0 + 16 * mb + (l & 15);
-          af[s][mb] = load_a_fp8_contig(a, lda, m, M, ks * 128 + 32 * g);
-          sa[s][mb] = m < M ? as[m * asm_ + ks * asg] : 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (base + s < kend) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const v4f t = mfma_fp8(wf[s], af[s][mb], v4f{0, 0, 0, 0});
-          const float f = sa[s][mb] * sw[s];
-          acc[mb] += t * f;
-        }
-      }
-    }
-  }
-  reduce_store<MB>(acc, red, nwaves, c, ldc, M, nt * 16, m0, nullptr);
-}
-
-// ---- MXFP4 W4A8 -------------------------------------------------------------
-// Same decomposition; K steps are handed out in groups of four so that a
-// wave's scale dword (four steps) is loaded once.  S is a multiple of 4.
-template <int MB, int S>
-__global__ __launch_bounds__(512) void k_w4a8_decode(const uint8_t* __restrict__ a, int64_t lda,
-                                                      const float* __restrict__ as, const uint8_t* __restrict__ w,
-                                                      const uint32_t* __restrict__ wsc, uint16_t* __restrict__ c,
-                                                      int64_t ldc, int M, int KS, int per) {
-  extern __shared__ float red[];
-  const int nt = blockIdx.x;
-  const int m0 = blockIdx.y * 16 * MB;
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int nwaves = blockDim.x >> 6;
-  const int g = l >> 4;
-  const int KQ = (KS + 3) >> 2;
-  const uint8_t* wt = w + static_cast<size_t>(nt) * KS * 1024 + l * 16;
-  const uint32_t* st = wsc + static_cast<size_t>(nt) * KQ * 64 + l;
-  v4f acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0, 0, 0, 0};
-  const int kbeg = wave * per;  // per is a multiple of 4
-  const int kend = min(kbeg + per, KS);
-  for (int base = kbeg; base < kend; base += S) {
-    v8i wf[S];
-    v8i af[S][MB];
-    uint32_t sd[S / 4];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int ks = base + s;
-      if (ks < kend) {
-        const uint4 x = *reinterpret_cast<const uint4*>(wt + static_cast<size_t>(ks) * 1024);
-        wf[s] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        if ((s & 3) == 0) sd[s >> 2] = st[static_cast<size_t>(ks >> 2) * 64];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[s][mb] = load_a_fp8_split(a, lda, m0 + 16 * mb + (l & 15), M, ks * 128, g);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (base + s < kend) {
-        const int sc = static_cast<int>(sd[s >> 2] >> (8 * (s & 3)));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_fp4w_fp8a(wf[s], af[s][mb], acc[mb], sc);
-      }
-    }
-  }
-  reduce_store<MB>(acc, red, nwaves, c, ldc, M, nt * 16, m0, as);
-}
-
-constexpr int kMaxWaves = 8;  // 512 threads: leaves 256 VGPRs per lane
-
-struct DecodeCfg {
-  int mb, s, sk, per;
+struct DecodeArgs {
+  const uint8_t* a;
+  int64_t lda;
+  const float* as;      // fp8: a_scale base; mx: per-token scale [M]
+  int64_t as_m, as_g;   // fp8 strides
+  const uint8_t* w;     // pre-laid-out codes
+  const float* wsf;     // fp8: w_scale [N/128, K/128]
+  const uint32_t* wsx;  // mx: e8m0 section
+  uint16_t* c;
+  int64_t ldc;
+  int M, N, KS;
+  int rs;               // activation rows staged per workgroup: min(M, 16*MB)
+  float* slab;          // [S][M][N] fp32 partials when gridDim.y > 1
+  int* counters;        // [gridDim.z][gridDim.x]
 };
 
-// Choose the m-tiles per workgroup, the steps per load batch and the number of
-// waves per workgroup (K split) for a small-M shape.
-DecodeCfg decode_cfg(int M, int KS, bool mx) {
+// Vector loads of the weight side issued after the activation DMA (the DMA is
+// complete once at most this many loads are outstanding).
+template <bool MX, int T, int R>
+constexpr int weight_loads() {
+  return MX ? T * R + T * ((R + 3) / 4) : 2 * T * R + 1;
+}
+
+// grid (ceil(N/16 / (TW*T)), S, ceil(M / (16*MB))); TW*KW waves.
+// Workgroup (x, y, z) covers n-tiles [x*TW*T, (x+1)*TW*T) over the K steps
+// [y*KW*R, (y+1)*KW*R) for activation rows [16*MB*z, 16*MB*(z+1)).  Wave
+// (tw, kw) owns T of the tiles over the kw-th run of R steps; the KW partial
+// sums of a tile are added through LDS in kw order.
+// LDS: the activation slice (KW*R steps x rs rows x 128 B, as 16-byte chunks)
+// and, for block-FP8, its scales [KW*R][rs]; the cross-wave partials reuse the
+// slice after the MFMAs.
+template <bool MX, int MB, int TW, int KW, int T, int R>
+__global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int last;
+  constexpr int kThreads = TW * KW * 64;
+  constexpr int kSteps = KW * R;  // K steps per workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tw = wave % TW, kw = wave / TW;
+  const int l = threadIdx.x & 63, g = l >> 4;
+  const int split = blockIdx.y, S = gridDim.y;
+  const int m0 = blockIdx.z * 16 * MB;
+  const int KS = p.KS, RS = p.rs;
+  const int wg_k0 = split * kSteps;
+  const int wg_steps = min(kSteps, KS - wg_k0);
+  const int ks0 = wg_k0 + kw * R;
+  const int klast = min(ks0 + R, KS) - 1;  // >= 0; below ks0 for an idle wave
+  const int nsteps = klast - ks0 + 1;      // <= 0 for an idle wave
+  const int rows = min(RS, p.M - m0);
+  const int ntiles = p.N >> 4;
+  const int tile0 = (blockIdx.x * TW + tw) * T;
+  const int KQ = (KS + 3) >> 2;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int a_instr = (kSteps * RS * 8 + 63) >> 6;
+  float* s_as = reinterpret_cast<float*>(lds + a_instr * 1024);
+  float* s_red = reinterpret_cast<float*>(lds);  // reuses the slice once every wave is done with it
+
+  // ---- 1. activation slice -> LDS (direct DMA, every lane useful).  Chunk c
+  // (16 B) of row i of step r sits at position (r*RS + i)*8 + (c ^ (i & 7)), so
+  // the 16 rows of an MFMA fragment read spread over all LDS banks.  Positions
+  // past the slice, or rows past M in the last row block, re-read valid bytes
+  // that are never used.
+  {
+    const uint8_t* abase = p.a + static_cast<int64_t>(m0) * p.lda + static_cast<int64_t>(wg_k0) * 128;
+    for (int k = wave; k < a_instr; k += TW * KW) {
+      const int q = k * 64 + l;
+      const int r = min(q / (RS * 8), wg_steps - 1);
+      const int ii = (q >> 3) % RS;
+      const int i = min(ii, rows - 1);
+      const int c = (q & 7) ^ (ii & 7);
+      dma16(lds0 + k * 1024, abase, static_cast<uint32_t>(i * p.lda + r * 128 + c * 16));
+    }
+  }
+  // block-FP8 activation scales of the slice (written to LDS below)
+  constexpr int kSPer = (kSteps * 16 * MB + kThreads - 1) / kThreads;
+  float sv[kSPer];
+  if constexpr (!MX) {
+#pragma unroll
+    for (int j = 0; j < kSPer; ++j) {
+      const int e = min(static_cast<int>(threadIdx.x) + j * kThreads, kSteps * RS - 1);
+      const int r = min(e / RS, wg_steps - 1), i = min(e % RS, rows - 1);
+      sv[j] = p.as[(m0 + i) * p.as_m + (wg_k0 + r) * p.as_g];
+    }
+  }
+  // block-FP8 weight scales of the wave's T tiles x R steps, one per lane
+  // (read back per step with a lane broadcast)
+  float wsv = 0.0f;
+  if constexpr (!MX) {
+    static_assert(T * R <= 64, "one weight scale per lane");
+    const int j = min(l, T * R - 1);
+    const int tj = min(tile0 + j / R, ntiles - 1);
+    wsv = p.wsf[static_cast<size_t>(tj >> 3) * KS + min(ks0 + j % R, klast)];
+  }
+
+  // ---- 2. the wave's weight fragments (all R steps of its T tiles) ---------
+  v8i wf[T][R];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const size_t tile = static_cast<size_t>(min(tile0 + t, ntiles - 1)) * KS;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t ks = min(ks0 + r, klast);
+      if constexpr (MX) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p.w + (tile + ks) * 1024 + l * 16);
+        wf[t][r] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      } else {
+        const uint8_t* src = p.w + (tile + ks) * 2048 + l * 16;
+        wf[t][r] = pack8(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 1024));
+      }
+    }
+  }
+  // mx: one e8m0 dword per lane covers four steps (ks0 is a multiple of 4)
+  uint32_t sd[T][(R + 3) / 4];
+  if constexpr (MX) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int qd = 0; qd < (R + 3) / 4; ++qd)
+        sd[t][qd] = p.wsx[(static_cast<size_t>(min(tile0 + t, ntiles - 1)) * KQ + min((ks0 >> 2) + qd, klast >> 2)) * 64 + l];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!MX) {
+#pragma unroll
+    for (int j = 0; j < kSPer; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * kThreads;
+      if (e < kSteps * RS) s_as[e] = sv[j];
+    }
+  }
+  wait_vm<weight_loads<MX, T, R>()>();  // this wave's activation DMA has landed
+  __syncthreads();
+
+  // ---- 3. MFMA over the slice ---------------------------------------------
+  v4f acc[T][MB];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[t][mb] = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool on = r < nsteps;
+    v8i af[MB];
+    float sa[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 16 * mb + (l & 15);
+      const int rc = min(row, RS - 1);
+      const int c0 = MX ? g : 2 * g, c1 = MX ? 4 + g : 2 * g + 1;
+      const uint8_t* rb = lds + ((kw * R + r) * RS + rc) * 128;
+      const uint4 x = *reinterpret_cast<const uint4*>(rb + ((c0 ^ (rc & 7)) << 4));
+      const uint4 y = *reinterpret_cast<const uint4*>(rb + ((c1 ^ (rc & 7)) << 4));
+      const bool use = on && row < rows;
+      af[mb] = keep_if(pack8(x, y), use);
+      if constexpr (!MX) sa[mb] = use ? s_as[(kw * R + r) * RS + rc] : 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if constexpr (MX) {
+        const int sc = static_cast<int>(sd[t][r >> 2] >> (8 * (r & 3)));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[t][mb] = mfma_fp4w_fp8a(wf[t][r], af[mb], acc[t][mb], sc);
+      } else {
+        const float sw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsv), t * R + r));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const v4f tmp = mfma_fp8(wf[t][r], af[mb], v4f{0, 0, 0, 0});
+          acc[t][mb] += tmp * (sa[mb] * sw);
+        }
+      }
+    }
+  }
+
+  // ---- 4. add the KW partials of each tile in kw order ----------------------
+  if constexpr (KW > 1) {
+    constexpr int kPer = T * MB * 4;  // floats per lane
+    __syncthreads();  // the activation slice is dead from here on
+    if (kw > 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s_red[(((kw - 1) * TW + tw) * kPer + (t * MB + mb) * 4 + j) * 64 + l] = acc[t][mb][j];
+    }
+    __syncthreads();
+    if (kw == 0)
+#pragma unroll
+    for (int u = 1; u < KW; ++u)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[t][mb][j] += s_red[(((u - 1) * TW + tw) * kPer + (t * MB + mb) * 4 + j) * 64 + l];
+  }
+
+  // ---- 5. output: lane l holds C[m = l%16 (+16 mb)][n = 4(l/16) .. +3] -------
+  auto store_bf16x4 = [&](int m, int n, v4f v) {
+    const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p.c + m * p.ldc + n) = uint2{lo, hi};
+  };
+  // (waves with kw > 0 stay to the end: they take part in every barrier)
+  const bool owner = kw == 0;
+  if (S == 1) {
+    if (owner)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
+          if (m < p.M && tile0 + t < ntiles) store_bf16x4(m, n, MX ? acc[t][mb] * p.as[m] : acc[t][mb]);
+        }
+    return;
+  }
+  // Split K: fp32 partials, then the last workgroup of this tile group adds
+  // them in split order.  The partials are device-scope stores (written
+  // through to the device-coherent level) and are read back with device-scope
+  // loads, so the hand-off needs no cache maintenance: each wave waits for its
+  // stores to be acknowledged before the counter increment.  (A device-scope
+  // fence would write back and invalidate the L2 of every XCD that runs a
+  // split -- microseconds per workgroup.)
+  if (owner)
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
+      if (m < p.M && tile0 + t < ntiles) {
+        float* dst = p.slab + (static_cast<size_t>(split) * p.M + m) * p.N + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) __hip_atomic_store(dst + j, acc[t][mb][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  const int cidx = blockIdx.z * gridDim.x + blockIdx.x;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&p.counters[cidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+  __syncthreads();
+  if (!last || !owner) return;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
+      if (m < p.M && tile0 + t < ntiles) {
+        v4f sum = v4f{0, 0, 0, 0};
+        for (int b = 0; b < S; ++b) {
+          const float* src = p.slab + (static_cast<size_t>(b) * p.M + m) * p.N + n;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sum[j] += __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        store_bf16x4(m, n, MX ? sum * p.as[m] : sum);
+      }
+    }
+  if (threadIdx.x == 0) __hip_atomic_store(&p.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct DecodeCfg {
+  int mb, tw, kw, t, r, s, groups, mblocks, rs;
+};
+
+// LDS the hardware grants one workgroup, less this kernel's static part.
+constexpr size_t kMaxDecodeLds = 160 * 1024 - 256;
+
+// Tile-waves (TW), K-waves (KW), n-tiles per wave (T) and K steps per wave
+// (R) for a small-M shape; S workgroups split the rest of K.  Chosen from
+// sweeps of the decode shapes on MI355X: for M <= 16 the activation slice is
+// small, so one or two tiles per workgroup and many K-waves keep ~1600-5000
+// waves streaming; for larger M the slice (8 KiB per step at M = 64) is shared
+// by more tiles and fewer steps.  MXFP4 needs R % 4 == 0 (one e8m0 dword per
+// lane covers four steps).
+DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   DecodeCfg d{};
   d.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  d.s = d.mb == 1 ? 8 : 4;
-  int sk = (KS + d.s - 1) / d.s;
-  if (sk > kMaxWaves) sk = kMaxWaves;
-  if (sk < 1) sk = 1;
-  int per = (KS + sk - 1) / sk;
-  if (mx) per = (per + 3) / 4 * 4;
-  sk = (KS + per - 1) / per;
-  d.sk = sk;
-  d.per = per;
+  d.mblocks = (M + 16 * d.mb - 1) / (16 * d.mb);
+  d.rs = std::min(M, 16 * d.mb);
+  if (d.mb == 1) {
+    if (mx) { d.tw = 1; d.kw = 10; d.t = 1; d.r = 4; }
+    else    { d.tw = 1; d.kw = 8; d.t = KS <= 40 ? 2 : 1; d.r = 5; }
+  } else if (d.mb == 2) {
+    if (mx) { d.tw = 4; d.kw = 2; d.t = 1; d.r = 8; }
+    else    { d.tw = 4; d.kw = 4; d.t = 1; d.r = 4; }
+  } else {
+    if (mx) { d.tw = 4; d.kw = 2; d.t = 1; d.r = 8; }
+    else    { d.tw = 2; d.kw = 4; d.t = 1; d.r = 4; }
+  }
+  const int ntiles = N / 16;
+  d.groups = (ntiles + d.tw * d.t - 1) / (d.tw * d.t);
+  d.s = (KS + d.kw * d.r - 1) / (d.kw * d.r);
   return d;
+}
+
+size_t decode_lds_bytes(const DecodeCfg& d, bool mx) {
+  const int steps = d.kw * d.r;
+  const size_t a = static_cast<size_t>((steps * d.rs * 8 + 63) / 64) * 1024;
+  const size_t sc = mx ? 0 : static_cast<size_t>(steps) * d.rs * sizeof(float);
+  const size_t red = static_cast<size_t>(d.kw - 1) * d.tw * d.t * d.mb * 4 * 64 * sizeof(float);
+  return std::max(a + sc, red + sc);
 }
 
 }  // namespace
 
-// Internal entry points used by the ABI layer (gemm_abi.cpp).
-int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, int64_t asm_, int64_t asg,
-                               const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
-                               hipStream_t st) {
-  const int KS = K / 128;
-  const DecodeCfg d = decode_cfg(M, KS, false);
-  dim3 grid(N / 16, (M + 16 * d.mb - 1) / (16 * d.mb));
-  dim3 block(64 * d.sk);
-  const size_t lds = static_cast<size_t>(d.sk) * d.mb * 4 * 64 * sizeof(float);
-#define BS_FP8D(MB_, S_) \
-  k_fp8_block_decode<MB_, S_><<<grid, block, lds, st>>>(a, lda, as, asm_, asg, w, ws, c, ldc, M, KS, d.per)
-  if (d.mb == 1) BS_FP8D(1, 8);
-  else if (d.mb == 2) BS_FP8D(2, 4);
-  else BS_FP8D(4, 4);
-#undef BS_FP8D
+// Rows per launch: larger M runs as consecutive 64-row launches that share the
+// workspace (stream order keeps them apart), so the split-K slab stays small.
+constexpr int kDecodeRows = 64;
+
+size_t bs_decode_workspace(int M, int N, int K, bool mx) {
+  const int rows = std::min(M, kDecodeRows);
+  const DecodeCfg d = decode_cfg(rows, N, K / 128, mx);
+  if (d.s <= 1) return 0;
+  const size_t slab = static_cast<size_t>(d.s) * rows * N * sizeof(float);
+  return (slab + 255) / 256 * 256 + static_cast<size_t>(d.groups) * d.mblocks * sizeof(int);
+}
+
+namespace {
+
+int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
+  const DecodeCfg d = decode_cfg(p.M, p.N, p.KS, mx);
+  if (d.s > 1) {
+    p.slab = static_cast<float*>(ws);
+    const size_t off = (static_cast<size_t>(d.s) * p.M * p.N * sizeof(float) + 255) / 256 * 256;
+    p.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
+  }
+  p.rs = d.rs;
+  dim3 grid(d.groups, d.s, d.mblocks);
+  dim3 block(64 * d.tw * d.kw);
+  const size_t lds = decode_lds_bytes(d, mx);
+  if (lds > kMaxDecodeLds) return BS_ERR_SHAPE;  // a dispatch beyond the LDS size aborts the queue
+  // Each instantiation raises its dynamic-LDS limit once, before its first launch.
+#define BS_DEC(MX_, MB_, TW_, KW_, T_, R_)                                                                 \
+  do {                                                                                                     \
+    auto* fn = &k_decode<MX_, MB_, TW_, KW_, T_, R_>;                                                      \
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                  \
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,         \
+                                                       static_cast<int>(kMaxDecodeLds));                   \
+    if (attr != hipSuccess) return BS_ERR_LAUNCH;                                                          \
+    fn<<<grid, block, lds, st>>>(p);                                                                       \
+  } while (0)
+  if (mx) {
+    if (d.mb == 1) BS_DEC(true, 1, 1, 10, 1, 4);
+    else if (d.mb == 2) BS_DEC(true, 2, 4, 2, 1, 8);
+    else BS_DEC(true, 4, 4, 2, 1, 8);
+  } else {
+    if (d.mb == 1) {
+      if (d.t == 2) BS_DEC(false, 1, 1, 8, 2, 5);
+      else BS_DEC(false, 1, 1, 8, 1, 5);
+    } else if (d.mb == 2) {
+      BS_DEC(false, 2, 4, 4, 1, 4);
+    } else {
+      BS_DEC(false, 4, 2, 4, 1, 4);
+    }
+  }
+#undef BS_DEC
   return bs_launch_status();
 }
 
+}  // namespace
+
+// Internal entry points used by the ABI layer (gemm_abi.hip).
+int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, int64_t asm_, int64_t asg,
+                               const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
+                               void* work, hipStream_t st) {
+  for (int r0 = 0; r0 < M; r0 += kDecodeRows) {
+    DecodeArgs p{a + r0 * lda, lda, as + r0 * asm_, asm_, asg, w, ws, nullptr, c + r0 * ldc, ldc,
+                 std::min(kDecodeRows, M - r0), N, K / 128, 0, nullptr, nullptr};
+    const int st_ = launch_decode(false, p, work, st);
+    if (st_ != BS_OK) return st_;
+  }
+  return BS_OK;
+}
+
 int bs_launch_w4a8_decode(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                          uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st) {
-  const int KS = K / 128;
-  const DecodeCfg d = decode_cfg(M, KS, true);
-  dim3 grid(N / 16, (M + 16 * d.mb - 1) / (16 * d.mb));
-  dim3 block(64 * d.sk);
-  const size_t lds = static_cast<size_t>(d.sk) * d.mb * 4 * 64 * sizeof(float);
-#define BS_W4D(MB_, S_) k_w4a8_decode<MB_, S_><<<grid, block, lds, st>>>(a, lda, as, w, wsc, c, ldc, M, KS, d.per)
-  if (d.mb == 1) BS_W4D(1, 8);
-  else if (d.mb == 2) BS_W4D(2, 4);
-  else BS_W4D(4, 4);
-#undef BS_W4D
-  return bs_launch_status();
+                          uint16_t* c, int64_t ldc, int M, int N, int K, void* work, hipStream_t st) {
+  DecodeArgs p{a, lda, as, 0, 0, w, nullptr, wsc, c, ldc, M, N, K / 128, 0, nullptr, nullptr};
+  return launch_decode(true, p, work, st);
 }

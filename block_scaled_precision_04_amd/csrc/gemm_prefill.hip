@@ -61,25 +61,6 @@ struct PrefillCfg {
   static_assert(kTM >= 1 && kTN >= 1, "wave tile too small");
 };
 
-// Direct-to-LDS 16-byte load: lane i's 16 bytes from sbase + voff land at LDS
-// byte address lds_addr + 16*i.  Issued from inline assembly so that the
-// compiler does not serialise it against the LDS reads of other stages; the
-// kernel waits for these loads itself (vmcnt) before the barrier that
-// publishes a stage.
-BS_INLINE void dma16(uint32_t lds_addr, const void* sbase, uint32_t voff) {
-  // one wait state between the M0 write and the LDS-DMA that reads it
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff),
-               "s"(sbase)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads outstanding
-template <int N>
-BS_INLINE void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Tile t of the grouped raster: group_m m-tiles sweep the n-tiles together.
 BS_INLINE void tile_mn(int t, int m_tiles, int n_tiles, int group_m, int& mt, int& nt) {
   const int per_group = group_m * n_tiles;

@@ -57,6 +57,10 @@ def test_sizes(blib):
     off = (codes + 255) // 256 * 256
     assert blib.bs_prelayout_mxfp4_bytes(N, K) == off + (N // 16) * ((K // 128 + 3) // 4) * 256
     assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
+    assert blib.bs_workspace_bytes(1, 8, 5120, 17408) > 0     # long K: split across workgroups
+    assert blib.bs_workspace_bytes(2, 8, 17408, 17408) > 0
+    assert blib.bs_workspace_bytes(2, 65, 17408, 17408) == 0  # W4A8 above the decode band: tiled kernel
+    assert blib.bs_workspace_bytes(1, 8, 100, 5120) == 0      # N % 128 != 0 -> 0
     assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0
     assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
 
@@ -91,6 +95,13 @@ def test_gemm_argument_validation(blib):
     assert w4(N=250) == -2
     assert w4(desc=d) == -4
     assert w4(w=ctypes.c_void_p(0x10010)) == -3   # the pre-laid-out weight must be 256-byte aligned
+    # long K splits across workgroups: a missing or short workspace is refused before any launch
+    dk = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 17408, 256 * 17408, 0, 0, 256 * 17408)
+    assert fp8(K=17408, desc=dk, lda=17408) == -5
+    mk = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 17408, 256 * 8704, 256 * 8704, 256 * 544, 256 * 9248)
+    assert w4(K=17408, desc=mk) == -3             # lda 512 < K comes first
+    assert blib.bsgemm_w4a8_mxfp4(FAKE, 17408, FAKE, ctypes.byref(mk), FAKE, FAKE, 256, 8, 256, 17408,
+                                  None, 0, None) == -5
 
 
 def test_skinny_and_producer_validation(blib):

@@ -19,8 +19,12 @@ def _fp8_run(aq, asc, wq, wsc, col_major_scale=False):
     a_s = dev_f32(asc)
     if col_major_scale:       # same values, stored [K/128, M] and read through strides
         a_s = dev_f32(np.ascontiguousarray(asc.T)).t()
-    c = bs.bsgemm_fp8_block(dev_u8(aq), a_s, desc, pre, dev_f32(wsc))
+    M, K = aq.shape
+    ws = bs.alloc_workspace(bs.BS_OP_FP8_BLOCK, M, desc.N, K)
+    c = bs.bsgemm_fp8_block(dev_u8(aq), a_s, desc, pre, dev_f32(wsc), ws=ws)
+    c2 = bs.bsgemm_fp8_block(dev_u8(aq), a_s, desc, pre, dev_f32(wsc), ws=ws)   # workspace reused
     torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
     return host_bits16(c)
 
 
@@ -53,7 +57,13 @@ def test_fp8_block_edges(M, N, K):
 # ------------------------------------------------------------------ MXFP4 W4A8
 def _w4_run(aq, asc, wp, e, out=None):
     pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
-    c = bs.bsgemm_w4a8_mxfp4(dev_u8(aq), dev_f32(asc), desc, pre, out=out)
+    M, K = aq.shape
+    ws = bs.alloc_workspace(bs.BS_OP_W4A8_MXFP4, M, desc.N, K)
+    c = bs.bsgemm_w4a8_mxfp4(dev_u8(aq), dev_f32(asc), desc, pre, out=out, ws=ws)
+    if ws is not None:        # split-K: a second call on the same workspace gives the same bits
+        c2 = bs.bsgemm_w4a8_mxfp4(dev_u8(aq), dev_f32(asc), desc, pre, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
     torch.cuda.synchronize()
     return c
 
@@ -87,7 +97,7 @@ def test_w4a8_fused_chain_consumer_on_gpu_producer_output():
     for case, M in ((0, 8), (1, 4096)):
         y, r, w = synth.producer_raw(case, M, K)
         q, s, _ = bs.add_rms_quant_fp8(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
-        c = bs.bsgemm_w4a8_mxfp4(q, s, desc, pre)
+        c = bs.bsgemm_w4a8_mxfp4(q, s, desc, pre, ws=bs.alloc_workspace(bs.BS_OP_W4A8_MXFP4, M, N, K))
         torch.cuda.synchronize()
         qh, sh, ch = q.cpu().numpy(), s.cpu().numpy(), host_bits16(c)
         if M <= 8:
