@@ -50,12 +50,11 @@ namespace {
 BS_INLINE v8i pack8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
-BS_INLINE v8i keep_if(v8i v, bool keep) {
-  v8i z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = keep ? v[i] : 0;
-  return z;
-}
+// 16-byte chunk swizzle of an activation row in LDS: the 16 rows of an MFMA
+// fragment read the same chunk index, and this permutation spreads them over
+// distinct bank groups whether the LDS serves 8 or 16 lanes of a 128-bit read
+// per cycle.
+BS_INLINE int a_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 BS_INLINE v4f mfma_fp8(v8i w, v8i a, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, c, 0, 0, 0, 127, 0, 127);
 }
@@ -75,7 +74,7 @@ struct DecodeArgs {
   int64_t ldc;
   int M, N, KS;
   int rs;               // activation rows staged per workgroup: min(M, 16*MB)
-  float* slab;          // [S][M][N] fp32 partials when gridDim.y > 1
+  float* slab;          // fp32 partials in fragment order when gridDim.y > 1
   int* counters;        // [gridDim.z][gridDim.x]
 };
 
@@ -121,10 +120,9 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
   float* s_red = reinterpret_cast<float*>(lds);  // reuses the slice once every wave is done with it
 
   // ---- 1. activation slice -> LDS (direct DMA, every lane useful).  Chunk c
-  // (16 B) of row i of step r sits at position (r*RS + i)*8 + (c ^ (i & 7)), so
-  // the 16 rows of an MFMA fragment read spread over all LDS banks.  Positions
-  // past the slice, or rows past M in the last row block, re-read valid bytes
-  // that are never used.
+  // (16 B) of row i of step r sits at position (r*RS + i)*8 + (c ^ a_swz(i)).
+  // Positions past the slice, or rows past M in the last row block, re-read
+  // valid bytes that are never used.
   {
     const uint8_t* abase = p.a + static_cast<int64_t>(m0) * p.lda + static_cast<int64_t>(wg_k0) * 128;
     for (int k = wave; k < a_instr; k += TW * KW) {
@@ -132,7 +130,7 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
       const int r = min(q / (RS * 8), wg_steps - 1);
       const int ii = (q >> 3) % RS;
       const int i = min(ii, rows - 1);
-      const int c = (q & 7) ^ (ii & 7);
+      const int c = (q & 7) ^ a_swz(ii);
       dma16(lds0 + k * 1024, abase, static_cast<uint32_t>(i * p.lda + r * 128 + c * 16));
     }
   }
@@ -200,22 +198,23 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = v4f{0, 0, 0, 0};
+  // Lanes whose row is past M compute garbage in their own output column only
+  // (never stored), so only the steps past this wave's range need masking: a
+  // wave-uniform branch.
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool on = r < nsteps;
+    if (r >= nsteps) break;
     v8i af[MB];
     float sa[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int row = 16 * mb + (l & 15);
-      const int rc = min(row, RS - 1);
+      const int rc = min(16 * mb + (l & 15), RS - 1);
       const int c0 = MX ? g : 2 * g, c1 = MX ? 4 + g : 2 * g + 1;
       const uint8_t* rb = lds + ((kw * R + r) * RS + rc) * 128;
-      const uint4 x = *reinterpret_cast<const uint4*>(rb + ((c0 ^ (rc & 7)) << 4));
-      const uint4 y = *reinterpret_cast<const uint4*>(rb + ((c1 ^ (rc & 7)) << 4));
-      const bool use = on && row < rows;
-      af[mb] = keep_if(pack8(x, y), use);
-      if constexpr (!MX) sa[mb] = use ? s_as[(kw * R + r) * RS + rc] : 0.0f;
+      const uint4 x = *reinterpret_cast<const uint4*>(rb + ((c0 ^ a_swz(rc)) << 4));
+      const uint4 y = *reinterpret_cast<const uint4*>(rb + ((c1 ^ a_swz(rc)) << 4));
+      af[mb] = pack8(x, y);
+      if constexpr (!MX) sa[mb] = s_as[(kw * R + r) * RS + rc];
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -280,24 +279,29 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
     return;
   }
   // Split K: fp32 partials, then the last workgroup of this tile group adds
-  // them in split order.  The partials are device-scope stores (written
-  // through to the device-coherent level) and are read back with device-scope
-  // loads, so the hand-off needs no cache maintenance: each wave waits for its
-  // stores to be acknowledged before the counter increment.  (A device-scope
-  // fence would write back and invalidate the L2 of every XCD that runs a
-  // split -- microseconds per workgroup.)
+  // them in split order.  The partials keep the MFMA fragment order -- slot
+  // (split, z, x, tw, t, mb) holds 4 x 64 floats, element j of lane l at
+  // j*64 + l -- so every store and load instruction covers 256 contiguous
+  // bytes.  They are device-scope stores (written through to the
+  // device-coherent level) read back with device-scope loads, so the hand-off
+  // needs no cache maintenance: each wave waits for its stores to be
+  // acknowledged before the counter increment.  (A device-scope fence would
+  // write back and invalidate the L2 of every XCD that runs a split --
+  // microseconds per workgroup.)
+  auto frag = [&](int sp, int t, int mb) {
+    const size_t f = ((((static_cast<size_t>(sp) * gridDim.z + blockIdx.z) * gridDim.x + blockIdx.x) * TW + tw) * T + t) * MB + mb;
+    return p.slab + f * 256 + l;
+  };
   if (owner)
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
-      if (m < p.M && tile0 + t < ntiles) {
-        float* dst = p.slab + (static_cast<size_t>(split) * p.M + m) * p.N + n;
+      for (int mb = 0; mb < MB; ++mb) {
+        float* dst = frag(split, t, mb);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) __hip_atomic_store(dst + j, acc[t][mb][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int j = 0; j < 4; ++j)
+          __hip_atomic_store(dst + j * 64, acc[t][mb][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-    }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
   asm volatile("" ::: "memory");
@@ -311,16 +315,15 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
-      if (m < p.M && tile0 + t < ntiles) {
-        v4f sum = v4f{0, 0, 0, 0};
-        for (int b = 0; b < S; ++b) {
-          const float* src = p.slab + (static_cast<size_t>(b) * p.M + m) * p.N + n;
+      v4f sum = v4f{0, 0, 0, 0};
+      for (int b = 0; b < S; ++b) {
+        const float* src = frag(b, t, mb);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sum[j] += __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        store_bf16x4(m, n, MX ? sum * p.as[m] : sum);
+        for (int j = 0; j < 4; ++j)
+          sum[j] += __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
+      if (m < p.M && tile0 + t < ntiles) store_bf16x4(m, n, MX ? sum * p.as[m] : sum);
     }
   if (threadIdx.x == 0) __hip_atomic_store(&p.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -335,9 +338,9 @@ constexpr size_t kMaxDecodeLds = 160 * 1024 - 256;
 // Tile-waves (TW), K-waves (KW), n-tiles per wave (T) and K steps per wave
 // (R) for a small-M shape; S workgroups split the rest of K.  Chosen from
 // sweeps of the decode shapes on MI355X: for M <= 16 the activation slice is
-// small, so one or two tiles per workgroup and many K-waves keep ~1600-5000
+// small, so one or two tiles per workgroup and many K-waves keep thousands of
 // waves streaming; for larger M the slice (8 KiB per step at M = 64) is shared
-// by more tiles and fewer steps.  MXFP4 needs R % 4 == 0 (one e8m0 dword per
+// by 4-8 tiles over fewer steps.  MXFP4 needs R % 4 == 0 (one e8m0 dword per
 // lane covers four steps).
 DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   DecodeCfg d{};
@@ -346,13 +349,10 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   d.rs = std::min(M, 16 * d.mb);
   if (d.mb == 1) {
     if (mx) { d.tw = 1; d.kw = 10; d.t = 1; d.r = 4; }
-    else    { d.tw = 1; d.kw = 8; d.t = KS <= 40 ? 2 : 1; d.r = 5; }
-  } else if (d.mb == 2) {
-    if (mx) { d.tw = 4; d.kw = 2; d.t = 1; d.r = 8; }
-    else    { d.tw = 4; d.kw = 4; d.t = 1; d.r = 4; }
+    else    { d.tw = 2; d.kw = 8; d.t = 1; d.r = 5; }
   } else {
-    if (mx) { d.tw = 4; d.kw = 2; d.t = 1; d.r = 8; }
-    else    { d.tw = 2; d.kw = 4; d.t = 1; d.r = 4; }
+    if (mx) { d.tw = 8; d.kw = 1; d.t = 1; d.r = 8; }
+    else    { d.tw = 4; d.kw = 4; d.t = 1; d.r = 4; }
   }
   const int ntiles = N / 16;
   d.groups = (ntiles + d.tw * d.t - 1) / (d.tw * d.t);
@@ -374,12 +374,22 @@ size_t decode_lds_bytes(const DecodeCfg& d, bool mx) {
 // workspace (stream order keeps them apart), so the split-K slab stays small.
 constexpr int kDecodeRows = 64;
 
+namespace {
+size_t slab_bytes(const DecodeCfg& d) {
+  return static_cast<size_t>(d.s) * d.mblocks * d.groups * d.tw * d.t * d.mb * 256 * sizeof(float);
+}
+}  // namespace
+
 size_t bs_decode_workspace(int M, int N, int K, bool mx) {
-  const int rows = std::min(M, kDecodeRows);
-  const DecodeCfg d = decode_cfg(rows, N, K / 128, mx);
-  if (d.s <= 1) return 0;
-  const size_t slab = static_cast<size_t>(d.s) * rows * N * sizeof(float);
-  return (slab + 255) / 256 * 256 + static_cast<size_t>(d.groups) * d.mblocks * sizeof(int);
+  // the largest of the row chunks' needs: full 64-row chunks and the remainder
+  size_t need = 0;
+  for (int rows : {std::min(M, kDecodeRows), M > kDecodeRows ? M % kDecodeRows : 0}) {
+    if (rows <= 0) continue;
+    const DecodeCfg d = decode_cfg(rows, N, K / 128, mx);
+    if (d.s <= 1) continue;
+    need = std::max(need, (slab_bytes(d) + 255) / 256 * 256 + static_cast<size_t>(d.groups) * d.mblocks * sizeof(int));
+  }
+  return need;
 }
 
 namespace {
@@ -388,7 +398,7 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
   const DecodeCfg d = decode_cfg(p.M, p.N, p.KS, mx);
   if (d.s > 1) {
     p.slab = static_cast<float*>(ws);
-    const size_t off = (static_cast<size_t>(d.s) * p.M * p.N * sizeof(float) + 255) / 256 * 256;
+    const size_t off = (slab_bytes(d) + 255) / 256 * 256;
     p.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
   }
   p.rs = d.rs;
@@ -408,17 +418,12 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
   } while (0)
   if (mx) {
     if (d.mb == 1) BS_DEC(true, 1, 1, 10, 1, 4);
-    else if (d.mb == 2) BS_DEC(true, 2, 4, 2, 1, 8);
-    else BS_DEC(true, 4, 4, 2, 1, 8);
+    else if (d.mb == 2) BS_DEC(true, 2, 8, 1, 1, 8);
+    else BS_DEC(true, 4, 8, 1, 1, 8);
   } else {
-    if (d.mb == 1) {
-      if (d.t == 2) BS_DEC(false, 1, 1, 8, 2, 5);
-      else BS_DEC(false, 1, 1, 8, 1, 5);
-    } else if (d.mb == 2) {
-      BS_DEC(false, 2, 4, 4, 1, 4);
-    } else {
-      BS_DEC(false, 4, 2, 4, 1, 4);
-    }
+    if (d.mb == 1) BS_DEC(false, 1, 2, 8, 1, 5);
+    else if (d.mb == 2) BS_DEC(false, 2, 4, 4, 1, 4);
+    else BS_DEC(false, 4, 4, 4, 1, 4);
   }
 #undef BS_DEC
   return bs_launch_status();
