@@ -11,9 +11,14 @@
 // row and of each activation row (four 16x16x32 bf16 MFMAs' worth; both
 // operands use the same K order so the products pair exactly), the four waves
 // reduce through LDS, and when K is split over several workgroups the partial
-// tile goes to the workspace slab; the last workgroup to finish a tile (an
-// atomic counter) sums the KSPLIT partials in index order (deterministic),
-// writes bf16 and resets the counter to zero for the next call.
+// tile goes to the workspace slab in MFMA fragment order (every store and load
+// covers 256 contiguous bytes); the last workgroup to finish a tile (an atomic
+// counter) sums the KSPLIT partials in index order (deterministic), writes
+// bf16 and resets the counter to zero for the next call.  The hand-off uses
+// device-scope stores and loads of the partials and no device-scope fence (a
+// fence writes back and invalidates the L2 of the XCD on every workgroup).
+// Rows past M load row M-1 (unconditional loads) and only ever reach output
+// columns that are not stored.
 #include "common.h"
 
 namespace {
@@ -46,10 +51,10 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     for (int j = 0; j < 4; ++j) wv[j] = wr[j];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int m = 16 * mb + (l & 15);
+      const int m = min(16 * mb + (l & 15), M - 1);
       const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + k0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xv[mb][j] = m < M ? xr[j] : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) xv[mb][j] = xr[j];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -63,6 +68,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     for (int r = 0; r < 4; ++r) red[wave][mb * 4 + r][l] = acc[mb][r];
   __syncthreads();
   // Thread o of the workgroup owns output o = (mb, r, lane): m = 16mb + lane%16, n = 4(lane/16) + r.
+  const int ntiles = gridDim.x;
   for (int o = threadIdx.x; o < MB * 256; o += 256) {
     const int lane = o & 63, rr = (o >> 6) & 3, mb = o >> 8;
     float s = 0.0f;
@@ -71,35 +77,47 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
     if (ksplit == 1) {
       if (m < M) c[m * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
-    } else if (m < M) {
-      slab[(static_cast<size_t>(kb) * M + m) * N + n] = s;
+    } else {
+      __hip_atomic_store(&slab[(static_cast<size_t>(kb) * ntiles + nt) * (MB * 256) + o], s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (ksplit == 1) return;
-  __threadfence();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partials are acknowledged
+  asm volatile("" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(&counters[nt], 1) == ksplit - 1);
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&counters[nt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ksplit - 1;
   __syncthreads();
   if (!last) return;
-  __threadfence();
-  for (int o = threadIdx.x; o < M * 16; o += 256) {
-    const int m = o >> 4, n = nt * 16 + (o & 15);
+  for (int o = threadIdx.x; o < MB * 256; o += 256) {
+    const int lane = o & 63, rr = (o >> 6) & 3, mb = o >> 8;
     float s = 0.0f;
-    for (int b = 0; b < ksplit; ++b) s += __builtin_nontemporal_load(&slab[(static_cast<size_t>(b) * M + m) * N + n]);
-    c[m * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
+    for (int b = 0; b < ksplit; ++b)
+      s += __hip_atomic_load(&slab[(static_cast<size_t>(b) * ntiles + nt) * (MB * 256) + o], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
+    if (m < M) c[m * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
   }
-  if (threadIdx.x == 0) counters[nt] = 0;
+  if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 int bs_skinny_ksplit(int K) { return (K / kChunk + kWaves - 1) / kWaves; }
 
+namespace {
+int skinny_mb(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+size_t skinny_slab_bytes(int M, int N, int ks) {
+  return static_cast<size_t>(ks) * (N / 16) * skinny_mb(M) * 256 * sizeof(float);
+}
+}  // namespace
+
 size_t bs_skinny_workspace(int M, int N, int K) {
   const int ks = bs_skinny_ksplit(K);
   if (ks <= 1) return 0;
-  const size_t slab = static_cast<size_t>(ks) * M * N * sizeof(float);
-  return (slab + 255) / 256 * 256 + static_cast<size_t>(N / 16) * sizeof(int);
+  return (skinny_slab_bytes(M, N, ks) + 255) / 256 * 256 + static_cast<size_t>(N / 16) * sizeof(int);
 }
 
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
@@ -109,7 +127,7 @@ int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, i
   int* counters = nullptr;
   if (ks > 1) {
     slab = static_cast<float*>(ws);
-    const size_t off = (static_cast<size_t>(ks) * M * N * sizeof(float) + 255) / 256 * 256;
+    const size_t off = (skinny_slab_bytes(M, N, ks) + 255) / 256 * 256;
     counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
   }
   dim3 grid(N / 16, ks);
