@@ -139,7 +139,12 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
  * w_pre:   the weight pre-laid-out by bs_prelayout_fp8_block (desc wd).
  * w_scale: fp32 [N/128, K/128] row-major, one multiplicative scale per block.
  * c:       bf16 [M, N], leading dimension ldc (elements, multiple of 4).
- * Needs M >= 1, N % 128 == 0, K % 128 == 0; a, c and w_pre 16-byte aligned. */
+ * ws:      bs_workspace_bytes(BS_OP_FP8_BLOCK, M, N, K) bytes (256-byte
+ *          aligned, zeroed once) when that is non-zero: K split across
+ *          workgroups; otherwise may be NULL.  M > 64 runs as consecutive
+ *          64-row launches on the stream, all sharing ws.
+ * Needs M >= 1, N % 128 == 0, K % 128 == 0, lda < 2^25; a, c and w_pre
+ * 16-byte aligned. */
 BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, int64_t as_stride_m,
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre,
                             const float* w_scale, void* c, int64_t ldc, int M, int N, int K,
@@ -151,8 +156,11 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
  * a: e4m3 [M, K] (lda bytes, multiple of 16); a_scale: fp32 [M];
  * w_pre: pre-laid-out by bs_prelayout_mxfp4 (desc wd); c: bf16 [M, N] (ldc
  * elements, multiple of 4).  Needs M >= 1, N % 16 == 0, K % 128 == 0.
- * Small M streams the weight (bandwidth-bound); large M runs the LDS-tiled
- * scaled-MFMA kernel (compute-bound). */
+ * Small M (<= 64) streams the weight (bandwidth-bound) and, when K is split
+ * across workgroups, needs ws of bs_workspace_bytes(BS_OP_W4A8_MXFP4, M, N, K)
+ * bytes (256-byte aligned, zeroed once); large M runs the LDS-tiled
+ * scaled-MFMA kernel (compute-bound) and needs no workspace.
+ * Needs M * lda < 2^32 and lda < 2^25 (32-bit activation offsets). */
 BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, const bs_wdesc* wd,
                              const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
                              size_t ws_bytes, bs_stream_t stream);
