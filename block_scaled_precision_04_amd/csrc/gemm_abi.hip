@@ -10,7 +10,8 @@ int bs_launch_w4a8_decode(const uint8_t* a, int64_t lda, const float* as, const 
                           uint16_t* c, int64_t ldc, int M, int N, int K, void* work, hipStream_t st);
 size_t bs_decode_workspace(int M, int N, int K, bool mx);
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                           uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st);
+                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, hipStream_t st);
+size_t bs_prefill_workspace(int M, int N, int K);
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
                      hipStream_t st);
 size_t bs_skinny_workspace(int M, int N, int K);
@@ -57,8 +58,8 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K) {
     return bs_decode_workspace(M, N, K, false);
   }
   if (op == BS_OP_W4A8_MXFP4) {
-    if (M < 1 || M > kW4A8DecodeMaxM || N < 16 || N % 16 || K < 128 || K % 128) return 0;
-    return bs_decode_workspace(M, N, K, true);
+    if (M < 1 || M > (1 << 22) || N < 16 || N % 16 || K < 128 || K % 128) return 0;
+    return M <= kW4A8DecodeMaxM ? bs_decode_workspace(M, N, K, true) : bs_prefill_workspace(M, N, K);
   }
   return 0;
 }
@@ -106,8 +107,10 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
     return bs_launch_w4a8_decode(static_cast<const uint8_t*>(a), lda, a_scale, w, wsc, static_cast<uint16_t*>(c),
                                  ldc, M, N, K, ws, st);
   }
+  const int wst = check_workspace(bs_prefill_workspace(M, N, K), ws, ws_bytes);
+  if (wst != BS_OK) return wst;
   return bs_launch_w4a8_prefill(static_cast<const uint8_t*>(a), lda, a_scale, w, wsc, static_cast<uint16_t*>(c),
-                                ldc, M, N, K, st);
+                                ldc, M, N, K, ws, st);
 }
 
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws, size_t ws_bytes,

@@ -31,6 +31,8 @@
 // one per XCD, and inside a chunk tiles follow a grouped raster (GROUP_M
 // m-tiles sweep the n-tiles together), so the workgroups resident on one XCD
 // at any moment share a few activation and weight tiles in that XCD's L2.
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
@@ -76,13 +78,21 @@ BS_INLINE void tile_mn(int t, int m_tiles, int n_tiles, int group_m, int& mt, in
 // sequence is cut into eight contiguous chunks, one per XCD, so the
 // workgroups resident on one XCD at any moment are neighbours in the grouped
 // raster and share activation / weight tiles in that XCD's L2.
-template <int BM, int BN, int WM, int WN, int OCC>
+// grid (tiles, S): workgroup (x, y) computes tile x over the y-th of S equal
+// runs of K steps; with S > 1 the partial tile goes to the workspace slab and
+// the last of the S workgroups of a tile adds them in split order.
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
-    const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m) {
+    const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m,
+    float* __restrict__ slab, int* __restrict__ counters) {
   using C = PrefillCfg<BM, BN, WM, WN>;
   constexpr int STAGES = 3;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage];
+  __shared__ int last;
+  const int S = SPLIT ? static_cast<int>(gridDim.y) : 1, sp = SPLIT ? static_cast<int>(blockIdx.y) : 0;
+  const int k_begin = SPLIT ? KS * sp / S : 0;   // KS < 2^24 (K < 2^31), so KS * S fits in 32 bits
+  const int k_end = SPLIT ? KS * (sp + 1) / S : KS;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
@@ -219,9 +229,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   //   for step s+3); refill Z with the first half of step s+1.
   // The next step uses (Z, X, Y).  The loads stay two steps ahead of their use.
 #pragma unroll
-  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, 0, 0);
+  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, k_begin, 0);
 #pragma unroll
-  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, min(1, KS - 1), 1);
+  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, min(k_begin + 1, k_end - 1), 1);
   wait_vm<C::kDmaMin>();
   __syncthreads();
   Frag f0, f1, f2;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     int pbuf = buf + 2;
     if (pbuf >= STAGES) pbuf -= STAGES;
     __builtin_amdgcn_sched_barrier(0);
-    mma(fx, sh, min(ks + 2, KS - 1), pbuf);
+    mma(fx, sh, min(ks + 2, k_end - 1), pbuf);
     __builtin_amdgcn_sched_barrier(0);
     lds_frags(st, 1, fy);
     __builtin_amdgcn_sched_barrier(0);
@@ -247,54 +257,134 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     // (after the last step this reads a buffer whose values are never used)
     lds_frags(lds + buf * C::kStage, 0, fz);
   };
-  int ks = 0;
-  for (; ks + 3 <= KS; ks += 3) {
+  int ks = k_begin;
+  for (; ks + 3 <= k_end; ks += 3) {
     step(ks, f0, f1, f2);
     step(ks + 1, f2, f0, f1);
     step(ks + 2, f1, f2, f0);
   }
-  if (ks < KS) step(ks++, f0, f1, f2);
-  if (ks < KS) step(ks++, f2, f0, f1);
+  if (ks < k_end) step(ks++, f0, f1, f2);
+  if (ks < k_end) step(ks++, f2, f0, f1);
   wait_vm<0>();
 
   // ---- epilogue: x per-token scale, bf16 RNE, 8-byte stores
+  auto store_tile = [&]() {
 #pragma unroll
-  for (int q = 0; q < C::kTM; ++q) {
-    const int m = m0 + arow[q];
-    if (m >= M) continue;
-    const float sc = as[m];
+    for (int q = 0; q < C::kTM; ++q) {
+      const int m = m0 + arow[q];
+      if (m >= M) continue;
+      const float sc = as[m];
 #pragma unroll
-    for (int p = 0; p < C::kTN; ++p) {
+      for (int p = 0; p < C::kTN; ++p) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wn * (BN / WN) + 32 * p + 8 * i + 4 * (l >> 5);
-        if (n < N) {
-          const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
-          const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
-          const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
-          const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
-          *reinterpret_cast<uint2*>(c + m * ldc + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        for (int i = 0; i < 4; ++i) {
+          const int n = n0 + wn * (BN / WN) + 32 * p + 8 * i + 4 * (l >> 5);
+          if (n < N) {
+            const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
+            const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
+            const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
+            const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
+            *reinterpret_cast<uint2*>(c + m * ldc + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          }
         }
       }
     }
+  };
+  if (!SPLIT || S == 1) {
+    store_tile();
+    return;
   }
+  // Split K: the fp32 partial tile in MFMA fragment order (element r of lane
+  // l of sub-tile (p, q) of wave w at ((w*kTN + p)*kTM + q)*1024 + r*64 + l),
+  // device-scope stores and loads, no cache maintenance -- the same hand-off
+  // as the decode GEMMs.
+  auto slot = [&](int b, int p, int q) {
+    const size_t t = ((static_cast<size_t>(b) * gridDim.x + blockIdx.x) * C::kWaves + wave) * C::kTN + p;
+    return slab + (t * C::kTM + q) * 1024 + l;
+  };
+#pragma unroll
+  for (int p = 0; p < C::kTN; ++p)
+#pragma unroll
+    for (int q = 0; q < C::kTM; ++q) {
+      float* dst = slot(sp, p, q);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __hip_atomic_store(dst + r * 64, acc[p][q][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+  __syncthreads();
+  if (!last) return;
+#pragma unroll
+  for (int p = 0; p < C::kTN; ++p)
+#pragma unroll
+    for (int q = 0; q < C::kTM; ++q) {
+      acc[p][q] = v16f{};
+      for (int b = 0; b < S; ++b) {
+        const float* src = slot(b, p, q);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[p][q][r] += __hip_atomic_load(src + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  store_tile();
+  if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int WM, int WN, int OCC>
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT>
 int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint8_t* wsc, uint16_t* c,
-               int64_t ldc, int M, int N, int KS, int group_m, hipStream_t st) {
+               int64_t ldc, int M, int N, int KS, int group_m, int S, void* ws, hipStream_t st) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  k_w4a8_prefill<BM, BN, WM, WN, OCC><<<tiles, 64 * WM * WN, 0, st>>>(a, static_cast<int>(lda), as, w, wsc, c, ldc, M,
-                                                                    N, KS, group_m);
+  float* slab = nullptr;
+  int* counters = nullptr;
+  if (S > 1) {
+    slab = static_cast<float*>(ws);
+    counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) +
+                                      static_cast<size_t>(S) * tiles * BM * BN * sizeof(float));
+  }
+  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
+      a, static_cast<int>(lda), as, w, wsc, c, ldc, M, N, KS, group_m, slab, counters);
   return bs_launch_status();
+}
+
+// Tile and K-split choice.  256x256 tiles (one workgroup per CU) when the
+// grid has at least 384 of them (1.5 rounds of 256 CUs: fewer leave a costly
+// partial round, e.g. 320 tiles run 20% slower than 1280 128x128 tiles);
+// otherwise 128x128 (two per CU), and when even those leave most of the 512
+// workgroup slots empty, K is split so that about 512 workgroups run,
+// keeping at least 8 K steps (1024 K) per split.
+struct PrefillPlan {
+  bool big;
+  int s, tiles;
+};
+PrefillPlan prefill_plan(int M, int N, int K) {
+  const int KS = K / 128;
+  const int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 384) return {true, 1, big_tiles};
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int s = 1;
+  if (tiles < 384) s = std::max(1, std::min(512 / tiles, KS / 8));
+  s = std::min(s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
+  return {false, s, tiles};
 }
 
 }  // namespace
 
+size_t bs_prefill_workspace(int M, int N, int K) {
+  const PrefillPlan pl = prefill_plan(M, N, K);
+  if (pl.s <= 1) return 0;
+  return static_cast<size_t>(pl.s) * pl.tiles * 128 * 128 * sizeof(float) + static_cast<size_t>(pl.tiles) * sizeof(int);
+}
+
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                           uint16_t* c, int64_t ldc, int M, int N, int K, hipStream_t st) {
+                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
   const int KS = K / 128;
-  const long big_tiles = static_cast<long>((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 256) return launch_cfg<256, 256, 2, 2, 1>(a, lda, as, w, reinterpret_cast<const uint8_t*>(wsc), c, ldc, M, N, KS, 4, st);
-  return launch_cfg<128, 128, 2, 2, 2>(a, lda, as, w, reinterpret_cast<const uint8_t*>(wsc), c, ldc, M, N, KS, 4, st);
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(wsc);
+  const PrefillPlan pl = prefill_plan(M, N, K);
+  if (pl.big) return launch_cfg<256, 256, 2, 2, 1, false>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, 1, nullptr, st);
+  return launch_cfg<128, 128, 2, 2, 2, true>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, pl.s, ws, st);
 }

@@ -59,7 +59,8 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
     assert blib.bs_workspace_bytes(1, 8, 5120, 17408) > 0     # long K: split across workgroups
     assert blib.bs_workspace_bytes(2, 8, 17408, 17408) > 0
-    assert blib.bs_workspace_bytes(2, 65, 17408, 17408) == 0  # W4A8 above the decode band: tiled kernel
+    assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
+    assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K
     assert blib.bs_workspace_bytes(1, 8, 100, 5120) == 0      # N % 128 != 0 -> 0
     assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0
     assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
