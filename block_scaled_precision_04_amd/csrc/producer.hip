@@ -82,33 +82,44 @@ __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict_
   const int t = threadIdx.x;
   const int nch = K >> 3;
   const size_t base = static_cast<size_t>(row) * nch;
+  // Every load of the row -- y, the residual and gamma -- is issued before
+  // any arithmetic (clamped chunk index, masked afterwards), so the row costs
+  // one memory round trip before the reductions.
+  uint4 yv[NC], rv[NC], gv[NC];
+  bool live[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = c * kThreads + t;
+    live[c] = idx < nch;
+    const int ci = min(idx, nch - 1);
+    yv[c] = y[base + ci];
+    if constexpr (NORM) {
+      rv[c] = res[base + ci];
+      gv[c] = gamma[ci];
+    }
+  }
   float h[NC][8];
   double ss = 0.0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int idx = c * kThreads + t;
-    if (idx < nch) {
-      float a[8];
-      unpack8(y[base + idx], a);
-      if constexpr (NORM) {
-        float b[8];
-        unpack8(res[base + idx], b);
-        uint32_t rb[8];
+    float a[8];
+    unpack8(yv[c], a);
+    if constexpr (NORM) {
+      float b[8];
+      unpack8(rv[c], b);
+      uint32_t rb[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          rb[j] = f32_to_bf16_rne(a[j] + b[j]);
-          h[c][j] = __uint_as_float(rb[j] << 16);
-          ss += static_cast<double>(h[c][j]) * static_cast<double>(h[c][j]);
-        }
-        rout[base + idx] = make_uint4(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16),
-                                      rb[4] | (rb[5] << 16), rb[6] | (rb[7] << 16));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) h[c][j] = a[j];
+      for (int j = 0; j < 8; ++j) {
+        rb[j] = f32_to_bf16_rne(a[j] + b[j]);
+        h[c][j] = live[c] ? __uint_as_float(rb[j] << 16) : 0.0f;
+        ss += static_cast<double>(h[c][j]) * static_cast<double>(h[c][j]);
       }
+      if (live[c])
+        rout[base + c * kThreads + t] = make_uint4(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16),
+                                                   rb[4] | (rb[5] << 16), rb[6] | (rb[7] << 16));
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[c][j] = 0.0f;
+      for (int j = 0; j < 8; ++j) h[c][j] = live[c] ? a[j] : 0.0f;
     }
   }
   if constexpr (NORM) {
@@ -116,14 +127,11 @@ __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict_
     const double inv = 1.0 / sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int idx = c * kThreads + t;
-      if (idx < nch) {
-        float g[8];
-        unpack8(gamma[idx], g);
+      float g[8];
+      unpack8(gv[c], g);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          h[c][j] = static_cast<float>(static_cast<double>(h[c][j]) * inv * (1.0 + static_cast<double>(g[j])));
-      }
+      for (int j = 0; j < 8; ++j)
+        h[c][j] = static_cast<float>(static_cast<double>(h[c][j]) * inv * (1.0 + static_cast<double>(g[j])));
     }
   }
   float amax = 0.0f;
