@@ -81,7 +81,7 @@ BS_INLINE void tile_mn(int t, int m_tiles, int n_tiles, int group_m, int& mt, in
 // grid (tiles, S): workgroup (x, y) computes tile x over the y-th of S equal
 // runs of K steps; with S > 1 the partial tile goes to the workspace slab and
 // the last of the S workgroups of a tile adds them in split order.
-template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT>
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m,
@@ -217,7 +217,46 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       if (dks >= 0) dma_one(i, dks, dbuf);
   };
 
-  // Pipeline: three LDS buffers (buffer of step s = s % 3) and three fragment
+  // one LDS read "piece" of a fragment set: pieces 0..kTN-1 are the weight
+  // fragments (+ e8m0 dword), kTN..kTN+kTM-1 the activation fragments
+  auto lds_piece = [&](const uint8_t* st, int hh, Frag& f, int i) {
+    if (i < C::kTN) {
+      const int p = i;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + boff[p][hh]);
+      f.b[p] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      f.s[p] = *reinterpret_cast<const uint32_t*>(st + soff[p][hh]);
+    } else {
+      const int q = i - C::kTN;
+      const int r = arow[q];
+      const int c0 = 4 * hh + (l >> 5);
+      const uint4 u = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0));
+      const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0 + 2));
+      f.a[q] = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    }
+  };
+  // MFMAs of one half step; after MFMA i, DMA i of step dks (if dks >= 0)
+  // and LDS-read piece i of the set rf (from stage rst, half rhh)
+  auto mma_il = [&](const Frag& f, int sh, int dks, int dbuf, const uint8_t* rst, int rhh, Frag& rf) {
+#pragma unroll
+    for (int p = 0; p < C::kTN; ++p) {
+      const int sc = static_cast<int>(f.s[p] >> sh);
+#pragma unroll
+      for (int q = 0; q < C::kTM; ++q) {
+        acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[p], f.a[q], acc[p][q], 4, 0, 0, sc, 0, 127);
+        const int i = p * C::kTM + q;
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < C::kDmaAll && dks >= 0) dma_one(i, dks, dbuf);
+        if (i < C::kTN + C::kTM) lds_piece(rst, rhh, rf, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int i = C::kTN * C::kTM; i < C::kDmaAll; ++i)
+      if (dks >= 0) dma_one(i, dks, dbuf);
+#pragma unroll
+    for (int i = C::kTN * C::kTM; i < C::kTN + C::kTM; ++i) lds_piece(rst, rhh, rf, i);
+  };
+  // Pipeline (the plain schedule, used with the 128x128 tile): three LDS buffers (buffer of step s = s % 3) and three fragment
   // register sets rotating over the 64-K halves.  The matrix unit queues a
   // wave's MFMAs and reads their operand registers only when each one starts,
   // so a register set is refilled only once the MFMAs that read it are two
@@ -257,14 +296,45 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     // (after the last step this reads a buffer whose values are never used)
     lds_frags(lds + buf * C::kStage, 0, fz);
   };
+  // The interleaved schedule (IL, used with the 256x256 tile), step s: this
+  // wave's loads of step s+1 landed and its LDS reads done ->
+  // barrier (step s+1 published, buffer s-1 free) -> MFMAs of the first half
+  // of s, interleaved with the loads of step s+2 (into buffer s-1) and the LDS
+  // reads of the second half of s -> MFMAs of the second half, interleaved
+  // with the LDS reads of the first half of s+1.
+  auto step2 = [&](int ks, Frag& fx, Frag& fy, Frag& fz) {
+    const int sh = 8 * (ks & 3);
+    const int b0 = (ks - k_begin) % STAGES;
+    const int b1 = b0 + 1 == STAGES ? 0 : b0 + 1;
+    const int b2 = b1 + 1 == STAGES ? 0 : b1 + 1;
+    wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    mma_il(fx, sh, min(ks + 2, k_end - 1), b2, lds + b0 * C::kStage, 1, fy);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_il(fy, sh, -1, 0, lds + b1 * C::kStage, 0, fz);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   int ks = k_begin;
-  for (; ks + 3 <= k_end; ks += 3) {
-    step(ks, f0, f1, f2);
-    step(ks + 1, f2, f0, f1);
-    step(ks + 2, f1, f2, f0);
+  if constexpr (IL) {
+    for (; ks + 3 <= k_end; ks += 3) {
+      step2(ks, f0, f1, f2);
+      step2(ks + 1, f2, f0, f1);
+      step2(ks + 2, f1, f2, f0);
+    }
+    if (ks < k_end) step2(ks++, f0, f1, f2);
+    if (ks < k_end) step2(ks++, f2, f0, f1);
+    (void)buf;
+  } else {
+    for (; ks + 3 <= k_end; ks += 3) {
+      step(ks, f0, f1, f2);
+      step(ks + 1, f2, f0, f1);
+      step(ks + 2, f1, f2, f0);
+    }
+    if (ks < k_end) step(ks++, f0, f1, f2);
+    if (ks < k_end) step(ks++, f2, f0, f1);
   }
-  if (ks < k_end) step(ks++, f0, f1, f2);
-  if (ks < k_end) step(ks++, f2, f0, f1);
   wait_vm<0>();
 
   // ---- epilogue: x per-token scale, bf16 RNE, 8-byte stores
@@ -335,7 +405,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT>
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL>
 int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint8_t* wsc, uint16_t* c,
                int64_t ldc, int M, int N, int KS, int group_m, int S, void* ws, hipStream_t st) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -346,7 +416,7 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
     counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) +
                                       static_cast<size_t>(S) * tiles * BM * BN * sizeof(float));
   }
-  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
+  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
       a, static_cast<int>(lda), as, w, wsc, c, ldc, M, N, KS, group_m, slab, counters);
   return bs_launch_status();
 }
@@ -385,6 +455,6 @@ int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const
   const int KS = K / 128;
   const uint8_t* sc = reinterpret_cast<const uint8_t*>(wsc);
   const PrefillPlan pl = prefill_plan(M, N, K);
-  if (pl.big) return launch_cfg<256, 256, 2, 2, 1, false>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, 1, nullptr, st);
-  return launch_cfg<128, 128, 2, 2, 2, true>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, pl.s, ws, st);
+  if (pl.big) return launch_cfg<256, 256, 2, 2, 1, false, true>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, 1, nullptr, st);
+  return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, pl.s, ws, st);
 }
