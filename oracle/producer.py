@@ -1,4 +1,5 @@
-"""The fused producer: residual add -> Gemma RMSNorm -> per-token e4m3 quant.
+"""The fused producers: residual add -> Gemma RMSNorm -> per-token e4m3 quant,
+and SiLU(gate) * up -> per-token e4m3 quant.
 
 Test infrastructure (see the package docstring); never used by the product path.
 
@@ -49,3 +50,37 @@ def add_rms_quant(y_bits, res_bits, w_bits, eps=1e-6, return_h=False):
     if return_h:
         return q, s, r_bits, h
     return q, s, r_bits
+
+
+def silu_mul_quant(gu_bits, return_h=False):
+    """The activation producer: SiLU(gate) * up, then the per-token e4m3 quant.
+
+    Source: radiance_arnq.py page, the ``silu_mul_quant`` custom op and the
+    ``_SiluMulQuant`` module that replaces the MLP's SiluAndMul ahead of the
+    down projection: input gu bf16 [M, 2N], outputs (q e4m3 [M, N], scale fp32
+    [M]) under the same per-token quant contract as the norm producer.
+
+    Steps, with the readings this oracle takes:
+      1. gate = gu[:, :N], up = gu[:, N:] (the first half is the activation's
+         input, as in the SiluAndMul convention the op replaces).
+      2. h = gate / (1 + exp(-gate)) * up in fp64 (SiLU(x) = x * sigmoid(x)),
+         from the bf16-decoded inputs.  No rounding of h to bf16: the fused
+         op emits no bf16 hidden tensor.
+      3. h32 = fp32(h), then the per-token quant of quant.py on h32:
+         scale = fp32(max(amax/448, 1/(448*512))), q = e4m3(clamp(h32/scale)).
+    A gate of 0 gives h = 0; a row of zeros gives scale 1/(448*512), q = 0.
+    """
+    gu = decode_bf16(gu_bits)
+    M, N2 = gu.shape
+    if N2 % 2:
+        raise ValueError("gu must have an even number of columns")
+    N = N2 // 2
+    gate, up = gu[:, :N], gu[:, N:]                               # step 1
+    with np.errstate(over="ignore"):
+        h = gate / (1.0 + np.exp(-gate)) * up                     # step 2
+    h32 = h.astype(np.float32)
+    s = scale_from_amax(np.abs(h32).astype(np.float64).max(axis=1))   # step 3
+    q = quant_with_scale(h32, s[:, None])
+    if return_h:
+        return q, s, h
+    return q, s

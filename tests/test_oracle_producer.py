@@ -155,3 +155,85 @@ def test_quant_per_token_and_group_fixtures():
     qt, st = quant.quant_per_token_bf16(tiny)
     assert float(st[0]) == float(np.float32(1.0 / (448 * 512)))
     assert np.all(codecs.decode_e4m3(qt) * float(st[0]) <= 2e-7)
+
+
+# ----------------------------------------------------------------- silu_mul_quant
+def _decimal_silu_row(g_bits, u_bits):
+    """SiLU(gate) * up at 60 digits with Decimal's own exp: an evaluation that
+    shares nothing with numpy's exp."""
+    getcontext().prec = 60
+    G = [Decimal(Fraction(v).numerator) / Decimal(Fraction(v).denominator) for v in exact.bf16_values(g_bits)]
+    U = [Decimal(Fraction(v).numerator) / Decimal(Fraction(v).denominator) for v in exact.bf16_values(u_bits)]
+    return [gk / (1 + (-gk).exp()) * uk for gk, uk in zip(G, U)]
+
+
+def test_silu_mul_quant_decimal_brute_force():
+    g = np.random.default_rng(25)
+    M, N = 5, 64
+    gu = (g.standard_normal((M, 2 * N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gu[1, :8] = _bf16_bits([0.0, -0.0, 30.0, -30.0, 88.0, -88.0, 120.0, -120.0])
+    gu[2, :N] = _bf16_bits(list(g.standard_normal(N) * 8.0))   # saturated and vanishing SiLU
+    gu[4, N:] = _bf16_bits(list(g.standard_normal(N) * 1e-4))  # small up: tiny row maximum
+    q, s, h = producer.silu_mul_quant(gu, return_h=True)
+    assert q.shape == (M, N) and s.shape == (M,)
+    for m in range(M):
+        hd = _decimal_silu_row(gu[m, :N], gu[m, N:])
+        hm = np.array([float(x) for x in hd])
+        assert np.allclose(h[m], hm, rtol=1e-13, atol=1e-300)
+        amax = max(abs(x) for x in hd)
+        amax32 = Fraction(float(np.float32(float(amax))))
+        s_want = max(amax32 / 448, Fraction(1, 448 * 512))
+        assert Fraction(float(s[m])) == exact_fp32(s_want)
+        v = (hm.astype(np.float32) / np.float32(s[m])).astype(np.float64)
+        v = np.clip(v, -FP8_MAX, FP8_MAX)
+        for k in range(N):
+            assert Fraction(float(codecs.decode_e4m3(q[m, k]))) == exact.e4m3_round(Fraction(float(v[k])))
+
+
+def test_silu_mul_quant_closed_forms():
+    g = np.random.default_rng(26)
+    N = 256
+    up = (g.standard_normal((1, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    # gate = 30: sigmoid is 1 - 9.4e-14, below half an fp32 ulp, so fp32(h) is exactly 30 * up
+    # (an fp32 number: 8 + 5 significant bits); a swapped half would give 30 * SiLU(up) instead
+    gate = np.tile(_bf16_bits([30.0]), (1, N))
+    q, s, h = producer.silu_mul_quant(np.concatenate([gate, up], axis=1), return_h=True)
+    want = 30.0 * codecs.decode_bf16(up)
+    assert np.array_equal(h.astype(np.float32), want.astype(np.float32))
+    q2, s2 = quant.quant_per_token(want.astype(np.float32))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    # gate = 0: SiLU(0) = 0, the minimum scale and zero codes (negative zeros as 0x80 or 0)
+    q, s = producer.silu_mul_quant(np.concatenate([np.zeros((1, N), np.uint16), up], axis=1))
+    assert np.all((q & 0x7F) == 0) and float(s[0]) == float(np.float32(1.0 / (448 * 512)))
+    # up = 1: h is SiLU itself; SiLU(x) - SiLU(-x) = x and SiLU(x) + SiLU(-x) = x * tanh(x / 2)
+    x = (g.standard_normal((1, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    one = np.tile(_bf16_bits([1.0]), (1, N))
+    _, _, hp = producer.silu_mul_quant(np.concatenate([x, one], axis=1), return_h=True)
+    _, _, hn = producer.silu_mul_quant(np.concatenate([x ^ np.uint16(0x8000), one], axis=1), return_h=True)
+    xv = codecs.decode_bf16(x)
+    assert np.allclose(hp - hn, xv, rtol=1e-14, atol=1e-15)
+    assert np.allclose(hp + hn, xv * np.tanh(xv / 2), rtol=1e-13, atol=1e-15)
+    # the logistic function from scipy: SiLU(x) = x * expit(x)
+    from scipy.special import expit
+    assert np.allclose(hp, xv * expit(xv), rtol=1e-14, atol=0)
+    # large negative gate: SiLU vanishes, the row maximum comes from the other columns
+    gate = np.tile(_bf16_bits([-60.0]), (1, N))
+    gate[0, 5] = _bf16_bits([2.0])[0]
+    q, s, h = producer.silu_mul_quant(np.concatenate([gate, one], axis=1), return_h=True)
+    assert q[0, 5] == 0x7E and np.all((np.delete(q[0], 5) & 0x7F) == 0)
+    h2 = np.float32(2.0 / (1.0 + float((-Decimal(2)).exp())))
+    assert float(s[0]) == float(np.float32(float(h2) / 448.0))       # amax rounded to fp32 first
+
+
+def test_silu_mul_quant_dequant_bound():
+    g = np.random.default_rng(27)
+    M, N = 16, 2048
+    gu = (g.standard_normal((M, 2 * N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q, s, h = producer.silu_mul_quant(gu, return_h=True)
+    assert np.all(np.any((q & 0x7F) == 0x7E, axis=1))
+    sd = s.astype(np.float64)[:, None]
+    deq = codecs.decode_e4m3(q) * sd
+    v = np.abs(h) / sd
+    e = np.maximum(np.floor(np.log2(np.maximum(v, 2.0 ** -6))), -6)
+    half_ulp = np.exp2(e - 3) / 2
+    assert np.all(np.abs(deq - h) / sd <= half_ulp + 1e-6 * v)
