@@ -58,6 +58,7 @@ SIGNATURES = {
     "bsgemm_w4a8_mxfp4": (_I, [_P, _L, _P, _D, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "gemm_bf16_skinny": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "add_rms_quant_fp8": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
+    "silu_mul_quant_fp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_per_token": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_group128": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_block128": (_I, [_P, _P, _P, _I, _I, _P]),
@@ -222,6 +223,17 @@ def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual
         _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
         M, K, _stream()))
     return q, scale, residual_out
+
+
+def silu_mul_quant_fp8(gu, q=None, scale=None):
+    """gu bf16 [M, 2N] (gate half first) -> (q e4m3 [M, N] as uint8, scale fp32 [M])."""
+    gu = _bits16(gu).contiguous()
+    M, N2 = gu.shape
+    N = N2 // 2
+    q = torch.empty((M, N), dtype=torch.uint8, device=gu.device) if q is None else q
+    scale = torch.empty((M,), dtype=torch.float32, device=gu.device) if scale is None else scale
+    _check("silu_mul_quant_fp8", lib().silu_mul_quant_fp8(_ptr(gu), _ptr(q), _ptr(scale), M, N, _stream()))
+    return q, scale
 
 
 def quant_fp8_per_token(x, q=None, scale=None):

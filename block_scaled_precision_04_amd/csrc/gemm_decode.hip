@@ -156,6 +156,7 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
   }
 
   // ---- 2. the wave's weight fragments (all R steps of its T tiles) ---------
+  // Every weight byte is read by exactly one wave: streaming loads.
   v8i wf[T][R];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -164,11 +165,12 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
     for (int r = 0; r < R; ++r) {
       const size_t ks = min(ks0 + r, klast);
       if constexpr (MX) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p.w + (tile + ks) * 1024 + l * 16);
+        const uint4 x = ld_stream16(reinterpret_cast<const uint4*>(p.w + (tile + ks) * 1024 + l * 16));
         wf[t][r] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
       } else {
         const uint8_t* src = p.w + (tile + ks) * 2048 + l * 16;
-        wf[t][r] = pack8(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 1024));
+        wf[t][r] = pack8(ld_stream16(reinterpret_cast<const uint4*>(src)),
+                         ld_stream16(reinterpret_cast<const uint4*>(src + 1024)));
       }
     }
   }

@@ -19,6 +19,9 @@ not used):
                     codes uniform bytes, e8m0 uniform in 117..130
   fused_chain       add + Gemma RMSNorm + per-token quant at K=5120,
                     M in {8,4096}, feeding W4A8 with N=17408
+  silu_chain        SiLU(gate) * up + per-token quant of the gate/up
+                    projection's output [M, 2*17408], M in {8,4096},
+                    feeding the W4A8 down projection (K=17408)
 Seeds: 100 * workload index + case index.
 """
 import numpy as np
@@ -31,6 +34,7 @@ WORKLOADS = {
     3: ("w4a8_prefill", [(m, n, k) for (n, k) in [(10240, 5120), (34816, 5120), (5120, 17408)]
                          for m in (256, 2048, 8192)]),
     4: ("fused_chain", [(8, 17408, 5120), (4096, 17408, 5120)]),
+    5: ("silu_chain", [(8, 17408), (4096, 17408)]),
 }
 
 
@@ -92,3 +96,9 @@ def producer_raw(case, M, K):
     """(y partial, residual, norm weight): bf16 N(0,1), N(0,1), N(0,0.1)."""
     g = rng(seed_of(4, case))
     return bf16_normal(g, (M, K), 1.0), bf16_normal(g, (M, K), 1.0), bf16_normal(g, (K,), 0.1)
+
+
+def silu_raw(case, M, N):
+    """gate/up projection output gu bf16 [M, 2N]: N(0,1) with 0.1% outliers x8."""
+    g = rng(seed_of(5, case))
+    return bf16_normal(g, (M, 2 * N), 1.0, outlier_p=0.001, outlier_factor=8.0)

@@ -21,7 +21,8 @@
  *                        permute_w, the per-token quant _traced_quant, the
  *                        decode split-K scratch);
  *   radiance_arnq.py     the fused residual add + Gemma RMSNorm + per-token
- *                        fp8 quant (ar_add_rms_quant, launch_add_rms_quant).
+ *                        fp8 quant (ar_add_rms_quant, launch_add_rms_quant) and
+ *                        the SiLU * up + quant producer (silu_mul_quant).
  *
  * Formats: e4m3 is OCP FP8 e4m3fn (max 448, no infinities); e2m1 is OCP FP4
  * packed two per byte, the even element in the low nibble; e8m0 is an MX
@@ -188,6 +189,20 @@ BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N,
 BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* gamma, float eps,
                              void* q, float* scale, void* residual_out, int M, int K,
                              bs_stream_t stream);
+
+/* SiLU(gate) * up + per-token e4m3 quant (radiance_arnq.py page, the
+ * silu_mul_quant op that replaces the MLP's SiluAndMul ahead of the down
+ * projection; the quant is the per-token rule above):
+ *   h = g / (1 + exp(-g)) * u,   g = gu[m, k], u = gu[m, N + k]
+ *   scale[m] = max(max_k |h| / 448, 1/(448*512))  (fp32)
+ *   q = e4m3(clamp(h / scale, +-448))
+ * gu: bf16 [M, 2N] contiguous (gate half first); q: e4m3 [M, N]; scale: fp32
+ * [M].  h is held in fp32 from the hardware exp2 and reciprocal and the codes
+ * use h * (1/scale): h is within a few fp32 ulps of the correctly rounded
+ * value, so a code may differ by one step where h/scale lies that close to a
+ * rounding midpoint.  N % 8 == 0, 8 <= N <= 32768; gu 16-byte aligned, q
+ * 8-byte aligned.  No overlap between gu and the outputs. */
+BS_API int silu_mul_quant_fp8(const void* gu, void* q, float* scale, int M, int N, bs_stream_t stream);
 
 /* Per-token e4m3 quant of bf16 rows (radiance_mxfp4.py page, _traced_quant):
  * scale[m] = max(max_k |x| / 448, 1/(448*512)); q = e4m3(clamp(x/scale)).

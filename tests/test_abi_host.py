@@ -29,6 +29,7 @@ def blib():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     for name in ("bsgemm_fp8_block", "bsgemm_w4a8_mxfp4", "gemm_bf16_skinny", "add_rms_quant_fp8",
+                 "silu_mul_quant_fp8",
                  "bs_prelayout_fp8_block", "bs_prelayout_mxfp4", "bs_unprelayout_fp8_block",
                  "bs_unprelayout_mxfp4", "bs_workspace_bytes"):
         assert name in syms
@@ -114,6 +115,11 @@ def test_skinny_and_producer_validation(blib):
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 65536, None) == -2
     assert blib.add_rms_quant_fp8(None, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5120, None) == -1
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, 8, 5120, None) == -7
+    assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 17404, None) == -2       # N % 8
+    assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 32776, None) == -2       # N above 32768
+    assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 0, 17408, None) == -2       # no rows
+    assert blib.silu_mul_quant_fp8(None, FAKE, FAKE, 8, 17408, None) == -1
+    assert blib.silu_mul_quant_fp8(ctypes.c_void_p(0x10008), FAKE, FAKE, 8, 17408, None) == -3
     assert blib.quant_fp8_group128(FAKE, FAKE, FAKE, 8, 5000, None) == -2
     assert blib.quant_fp8_block128(FAKE, FAKE, FAKE, 100, 512, None) == -2
 

@@ -76,3 +76,51 @@ def test_quant_group_and_block():
     q, s = bs.quant_fp8_block128(dev_bf16(w))
     qo, so = quant.quant_block128_bf16(w)
     checks.assert_codes_close(host_u8(q), s.cpu().numpy(), qo, so, "block128")
+
+
+# ----------------------------------------------------------------- silu_mul_quant
+def _run_silu(gu):
+    q, s = bs.silu_mul_quant_fp8(dev_bf16(gu))
+    torch.cuda.synchronize()
+    return host_u8(q), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("case,M", [(0, 8), (1, 4096)])
+def test_silu_mul_quant_down_projection_input(case, M):
+    """The down projection's input at its real width N = 17408; at M = 4096
+    the oracle takes every 16th row (rows are independent)."""
+    N = 17408
+    gu = synth.silu_raw(case, M, N)
+    qg, sg = _run_silu(gu)
+    rows = np.arange(0, M, 16) if M > 64 else np.arange(M)
+    qo, so = producer.silu_mul_quant(gu[rows])
+    print(checks.assert_codes_close(qg[rows], sg[rows], qo, so, f"silu_mul_quant M={M}"))
+
+
+@pytest.mark.parametrize("M,N", [(1, 8), (3, 136), (5, 2056), (2, 32768), (300, 1000), (257, 17400), (64, 8200)])
+def test_silu_mul_quant_ragged_shapes(M, N):
+    g = synth.rng(900 + N)
+    gu = synth.bf16_normal(g, (M, 2 * N), 1.5)
+    qg, sg = _run_silu(gu)
+    qo, so = producer.silu_mul_quant(gu)
+    checks.assert_codes_close(qg, sg, qo, so, f"silu_mul_quant M={M} N={N}")
+
+
+@pytest.mark.parametrize("M", [4, 512])
+def test_silu_mul_quant_special_rows(M):
+    """Zero rows, saturated gates (+-60), a single live column and tiny rows,
+    on both workgroup shapes (few rows / many rows)."""
+    N = 1024
+    g = synth.rng(31)
+    gu = synth.bf16_normal(g, (M, 2 * N), 1.0)
+    gu[0] = 0                                       # zero row: minimum scale, zero codes
+    gu[1, :N] = 0x4270                              # gate 60: h = 60 * up
+    gu[2, :N] = 0xC270                              # gate -60: h vanishes (min scale)
+    gu[3, :N] = 0xC270
+    gu[3, 17] = 0x4000                              # ... but for one column with gate 2
+    gu[3, N:] = 0x3F80                              # up = 1
+    qg, sg = _run_silu(gu)
+    qo, so = producer.silu_mul_quant(gu)
+    checks.assert_codes_close(qg, sg, qo, so, f"silu special rows M={M}")
+    assert np.all((qg[0] & 0x7F) == 0) and np.float32(sg[0]) == np.float32(1.0 / (448 * 512))
+    assert qg[3, 17] == 0x7E and np.all((np.delete(qg[3], 17) & 0x7F) == 0)
