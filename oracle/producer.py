@@ -32,21 +32,49 @@ from .codecs import decode_bf16, round_to_bf16
 from .quant import scale_from_amax, quant_with_scale
 
 
-def add_rms_quant(y_bits, res_bits, w_bits, eps=1e-6, return_h=False):
-    """y, residual bf16 [M, K]; w bf16 [K] -> (q uint8 [M,K], scale fp32 [M],
-    residual_out bf16 [M,K]) and, on request, h fp64 [M,K]."""
+def _add_rms(y_bits, res_bits, w_bits, eps):
+    """Steps 1-4: (residual_out bf16 bits, h fp64)."""
     y = decode_bf16(y_bits)
     res = decode_bf16(res_bits)
     w = decode_bf16(w_bits)
-    M, K = y.shape
     r_bits = round_to_bf16(y + res)                               # step 1
     r = decode_bf16(r_bits)
     ms = np.mean(r * r, axis=1, keepdims=True)                    # step 2
     inv = 1.0 / np.sqrt(ms + eps)                                 # step 3
     h = r * inv * (1.0 + w)[None, :]                              # step 4
+    return r_bits, h
+
+
+def add_rms_quant(y_bits, res_bits, w_bits, eps=1e-6, return_h=False):
+    """y, residual bf16 [M, K]; w bf16 [K] -> (q uint8 [M,K], scale fp32 [M],
+    residual_out bf16 [M,K]) and, on request, h fp64 [M,K]."""
+    r_bits, h = _add_rms(y_bits, res_bits, w_bits, eps)
     h32 = h.astype(np.float32)
     s = scale_from_amax(np.abs(h32).astype(np.float64).max(axis=1))   # step 5
     q = quant_with_scale(h32, s[:, None])                         # step 6
+    if return_h:
+        return q, s, r_bits, h
+    return q, s, r_bits
+
+
+def add_rms_quant_group128(y_bits, res_bits, w_bits, eps=1e-6, return_h=False):
+    """The norm producer for the block-FP8 consumer: steps 1-4 as above, then
+    the same quant rule per 128-wide group of each row instead of per row --
+    the activation format of the block-FP8 GEMM (radiance_kernels.py page:
+    one scale per token per 128 K, the ``_ps_cfg`` comment and
+    ``block_scaled_mm``).
+      5'. h32 = fp32(h); for each group g of columns 128g .. 128g+127:
+          scale[m, g] = fp32(max(amax_g/448, 1/(448*512)));
+      6'. q = e4m3(clamp(h32 / scale[m, g], +-448)).
+    Returns (q uint8 [M,K], scale fp32 [M, K/128], residual_out bf16 [M,K]).
+    """
+    r_bits, h = _add_rms(y_bits, res_bits, w_bits, eps)
+    M, K = h.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    hg = h.astype(np.float32).reshape(M, K // 128, 128)
+    s = scale_from_amax(np.abs(hg).astype(np.float64).max(axis=2))    # step 5'
+    q = quant_with_scale(hg, s[:, :, None]).reshape(M, K)             # step 6'
     if return_h:
         return q, s, r_bits, h
     return q, s, r_bits

@@ -237,3 +237,58 @@ def test_silu_mul_quant_dequant_bound():
     e = np.maximum(np.floor(np.log2(np.maximum(v, 2.0 ** -6))), -6)
     half_ulp = np.exp2(e - 3) / 2
     assert np.all(np.abs(deq - h) / sd <= half_ulp + 1e-6 * v)
+
+
+# ----------------------------------------------------------------- group-scale producer
+def test_group_producer_reduces_to_per_token_at_one_group():
+    g = np.random.default_rng(28)
+    y = (g.standard_normal((5, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    r = (g.standard_normal((5, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = ((g.standard_normal(128) * 0.1).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q1, s1, r1 = producer.add_rms_quant(y, r, w)
+    qg, sg, rg = producer.add_rms_quant_group128(y, r, w)
+    assert np.array_equal(q1, qg) and np.array_equal(s1, sg[:, 0]) and np.array_equal(r1, rg)
+
+
+def test_group_producer_decimal_brute_force():
+    g = np.random.default_rng(29)
+    M, K = 3, 384
+    y = (g.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    r = (g.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = ((g.standard_normal(K) * 0.1).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y[1, 128:256] = _bf16_bits(list(g.standard_normal(128) * 1e-3))   # a quiet group: its own small scale
+    q, s, rb = producer.add_rms_quant_group128(y, r, w)
+    _, _, rb1 = producer.add_rms_quant(y, r, w)
+    assert np.array_equal(rb, rb1) and s.shape == (M, K // 128)
+    for m in range(M):
+        hd, _ = _decimal_producer_row(y[m], r[m], w, 1e-6)
+        hm = np.array([float(x) for x in hd])
+        for gi in range(K // 128):
+            blk = hm[gi * 128:(gi + 1) * 128]
+            amax32 = Fraction(float(np.float32(float(max(abs(x) for x in hd[gi * 128:(gi + 1) * 128])))))
+            assert Fraction(float(s[m, gi])) == exact_fp32(max(amax32 / 448, Fraction(1, 448 * 512)))
+            v = np.clip((blk.astype(np.float32) / np.float32(s[m, gi])).astype(np.float64), -FP8_MAX, FP8_MAX)
+            for k in range(128):
+                assert Fraction(float(codecs.decode_e4m3(q[m, gi * 128 + k]))) == exact.e4m3_round(Fraction(float(v[k])))
+            assert (q[m, gi * 128:(gi + 1) * 128] & 0x7F).max() == 0x7E        # every group reaches the top code
+
+
+def test_group_producer_constant_rows_and_bound():
+    K = 512
+    y = np.tile(_bf16_bits([0.75]), (1, K))
+    y[0, 128:256] = _bf16_bits([-0.5])[0]
+    zeros = np.zeros((1, K), np.uint16)
+    q, s, _ = producer.add_rms_quant_group128(y, zeros, np.zeros(K, np.uint16))
+    assert np.all(q[0, :128] == 0x7E) and np.all(q[0, 128:256] == 0xFE) and np.all(q[0, 256:] == 0x7E)
+    assert s[0, 1] < s[0, 0] and s[0, 0] == s[0, 2] == s[0, 3]
+    g = np.random.default_rng(30)
+    M, K = 8, 1024
+    y = (g.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    r = (g.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = ((g.standard_normal(K) * 0.1).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q, s, _, h = producer.add_rms_quant_group128(y, r, w, return_h=True)
+    sd = np.repeat(s.astype(np.float64), 128, axis=1)
+    deq = codecs.decode_e4m3(q) * sd
+    v = np.abs(h) / sd
+    e = np.maximum(np.floor(np.log2(np.maximum(v, 2.0 ** -6))), -6)
+    assert np.all(np.abs(deq - h) / sd <= np.exp2(e - 3) / 2 + 1e-6 * v)
