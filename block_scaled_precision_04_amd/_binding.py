@@ -58,6 +58,7 @@ SIGNATURES = {
     "bsgemm_w4a8_mxfp4": (_I, [_P, _L, _P, _D, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "gemm_bf16_skinny": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "add_rms_quant_fp8": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
+    "add_rms_quant_fp8_group128": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
     "silu_mul_quant_fp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_per_token": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_group128": (_I, [_P, _P, _P, _I, _I, _P]),
@@ -220,6 +221,22 @@ def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual
     scale = torch.empty((M,), dtype=torch.float32, device=dev) if scale is None else scale
     residual_out = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if residual_out is None else residual_out
     _check("add_rms_quant_fp8", lib().add_rms_quant_fp8(
+        _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
+        M, K, _stream()))
+    return q, scale, residual_out
+
+
+def add_rms_quant_fp8_group128(y, residual, gamma, eps=1e-6, q=None, scale=None, residual_out=None):
+    """(q e4m3 [M,K] as uint8, scale fp32 [M, K/128], residual_out bf16 [M,K])."""
+    y = _bits16(y).contiguous()
+    residual = _bits16(residual).contiguous()
+    gamma = _bits16(gamma).contiguous()
+    M, K = y.shape
+    dev = y.device
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
+    scale = torch.empty((M, K // 128), dtype=torch.float32, device=dev) if scale is None else scale
+    residual_out = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if residual_out is None else residual_out
+    _check("add_rms_quant_fp8_group128", lib().add_rms_quant_fp8_group128(
         _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
         M, K, _stream()))
     return q, scale, residual_out

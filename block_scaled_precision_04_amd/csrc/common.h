@@ -91,11 +91,38 @@ BS_INLINE void dma16(uint32_t lds_addr, const void* sbase, uint32_t voff) {
                : "memory", "m0");
 }
 
+// The 4-byte form: lane i's dword from sbase + voff lands at lds_addr + 4*i.
+BS_INLINE void dma4(uint32_t lds_addr, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_addr), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads outstanding
 template <int N>
 BS_INLINE void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Output-tile order of the LDS-tiled GEMMs.  gfx950 hands workgroup b to XCD
+// b % 8, and each XCD has its own L2: the tile sequence is cut into eight
+// contiguous chunks, one per XCD, and inside a chunk the tiles follow a
+// grouped raster (group_m m-tiles sweep the n-tiles together), so the
+// workgroups resident on one XCD at any moment share a few activation and
+// weight tiles in that XCD's L2.  One workgroup per tile: b < m_tiles*n_tiles.
+constexpr int kXcds = 8;
+BS_INLINE void xcd_tile(int b, int m_tiles, int n_tiles, int group_m, int& mt, int& nt) {
+  const int T = m_tiles * n_tiles;
+  const int x = b % kXcds, jj = b / kXcds;
+  const int t = x * (T / kXcds) + min(x, T % kXcds) + jj;
+  const int per_group = group_m * n_tiles;
+  const int grp = t / per_group;
+  const int first_m = grp * group_m;
+  const int gsize = min(m_tiles - first_m, group_m);
+  const int loc = t - grp * per_group;
+  mt = first_m + loc % gsize;
+  nt = loc / gsize;
 }
 
 constexpr float kFp8Max = 448.0f;

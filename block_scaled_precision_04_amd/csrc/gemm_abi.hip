@@ -9,6 +9,10 @@ int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, i
 int bs_launch_w4a8_decode(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                           uint16_t* c, int64_t ldc, int M, int N, int K, void* work, hipStream_t st);
 size_t bs_decode_workspace(int M, int N, int K, bool mx);
+int bs_launch_fp8_block_prefill(const uint8_t* a, int64_t lda, const float* as, int64_t as_m, int64_t as_g,
+                                const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
+                                hipStream_t st);
+int bs_fp8_prefill_min_m();
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                            uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, hipStream_t st);
 size_t bs_prefill_workspace(int M, int N, int K);
@@ -55,7 +59,7 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K) {
   }
   if (op == BS_OP_FP8_BLOCK) {
     if (M < 1 || M > kFp8MaxM || N < 128 || N % 128 || K < 128 || K % 128) return 0;
-    return bs_decode_workspace(M, N, K, false);
+    return M >= bs_fp8_prefill_min_m() ? 0 : bs_decode_workspace(M, N, K, false);
   }
   if (op == BS_OP_W4A8_MXFP4) {
     if (M < 1 || M > (1 << 22) || N < 16 || N % 16 || K < 128 || K % 128) return 0;
@@ -78,6 +82,13 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
                bs_aligned(w_scale, 4),
            BS_ERR_ALIGN);
   BS_CHECK(as_stride_m >= 0 && as_stride_g >= 0, BS_ERR_ARG);
+  BS_CHECK(K < (1 << 24), BS_ERR_SHAPE);  // weight tiles are addressed with 32-bit offsets
+  // the tiled kernel addresses a tile's activation scales with 32-bit offsets
+  BS_CHECK(as_stride_m < (1 << 22), BS_ERR_SHAPE);
+  if (M >= bs_fp8_prefill_min_m())
+    return bs_launch_fp8_block_prefill(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,
+                                       static_cast<const uint8_t*>(w_pre), w_scale, static_cast<uint16_t*>(c), ldc,
+                                       M, N, K, static_cast<hipStream_t>(stream));
   const int wst = check_workspace(bs_decode_workspace(M, N, K, false), ws, ws_bytes);
   if (wst != BS_OK) return wst;
   return bs_launch_fp8_block_decode(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,

@@ -37,8 +37,6 @@
 
 namespace {
 
-constexpr int kXcds = 8;
-
 BS_INLINE int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
 template <int BM, int BN, int WM, int WN>
@@ -62,17 +60,6 @@ struct PrefillCfg {
   static_assert(kSStage % 1024 == 0, "scale stage must be whole waves");
   static_assert(kTM >= 1 && kTN >= 1, "wave tile too small");
 };
-
-// Tile t of the grouped raster: group_m m-tiles sweep the n-tiles together.
-BS_INLINE void tile_mn(int t, int m_tiles, int n_tiles, int group_m, int& mt, int& nt) {
-  const int per_group = group_m * n_tiles;
-  const int grp = t / per_group;
-  const int first_m = grp * group_m;
-  const int gsize = min(m_tiles - first_m, group_m);
-  const int loc = t - grp * per_group;
-  mt = first_m + loc % gsize;
-  nt = loc / gsize;
-}
 
 // One workgroup per output tile.  Workgroup b runs on XCD b % 8; the tile
 // sequence is cut into eight contiguous chunks, one per XCD, so the
@@ -101,11 +88,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   const int KQ = (KS + 3) >> 2;
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  const int T = m_tiles * n_tiles;
-  const int x = blockIdx.x % kXcds, jj = blockIdx.x / kXcds;
-  const int cq = T / kXcds, cr = T % kXcds;
   int mt, ntile;
-  tile_mn(x * cq + min(x, cr) + jj, m_tiles, n_tiles, group_m, mt, ntile);
+  xcd_tile(blockIdx.x, m_tiles, n_tiles, group_m, mt, ntile);
   const int m0 = mt * BM, n0 = ntile * BN;
   const int nt0 = n0 >> 4;
 

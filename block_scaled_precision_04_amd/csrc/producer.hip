@@ -72,7 +72,10 @@ BS_INLINE void unpack8(uint4 v, float* f) {
 }
 
 // NORM = true: add + RMSNorm + quant.  NORM = false: per-token quant of y.
-template <int NC, bool NORM>
+// GROUP = true: one scale per 128-wide group of the row instead of one per
+// row; chunk idx = c*256 + t belongs to group idx/16, so the 16 consecutive
+// threads holding a group reduce its maximum with four shuffles.
+template <int NC, bool NORM, bool GROUP = false>
 __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict__ y,
                                                         const uint4* __restrict__ res,
                                                         const uint4* __restrict__ gamma, float eps,
@@ -136,20 +139,39 @@ __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict_
         h[c][j] = static_cast<float>(static_cast<double>(h[c][j]) * inv * (1.0 + static_cast<double>(g[j])));
     }
   }
-  float amax = 0.0f;
+  if constexpr (GROUP) {
+    const int ngroups = nch >> 4;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
+      float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
-  amax = block_max(amax, red_f);
-  const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
-  if (t == 0) scale[row] = s;
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int idx = c * kThreads + t;
-    if (idx < nch) {
-      const uint2 v = quant8(h[c], s);
-      st_stream8(q + base + idx, v.x, v.y);
+      for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+      const int idx = c * kThreads + t;
+      if (idx < nch) {   // K % 128 == 0: a group's 16 threads are all live or all idle
+        if ((t & 15) == 0) scale[static_cast<size_t>(row) * ngroups + (idx >> 4)] = s;
+        const uint2 v = quant8(h[c], s);
+        st_stream8(q + base + idx, v.x, v.y);
+      }
+    }
+  } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
+    amax = block_max(amax, red_f);
+    const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+    if (t == 0) scale[row] = s;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = c * kThreads + t;
+      if (idx < nch) {
+        const uint2 v = quant8(h[c], s);
+        st_stream8(q + base + idx, v.x, v.y);
+      }
     }
   }
 }
@@ -295,13 +317,13 @@ int launch_silu_quant(const void* gu, void* q, float* scale, int M, int N, hipSt
   return bs_launch_status();
 }
 
-template <bool NORM>
+template <bool NORM, bool GROUP = false>
 int launch_row_quant(const void* y, const void* res, const void* gamma, float eps, void* q, float* scale,
                      void* rout, int M, int K, hipStream_t st) {
   const int nc = (K / 8 + kThreads - 1) / kThreads;
   dim3 grid(M), block(kThreads);
 #define BS_ROWQ(N_)                                                                                    \
-  k_row_quant<N_, NORM><<<grid, block, 0, st>>>(                                                        \
+  k_row_quant<N_, NORM, GROUP><<<grid, block, 0, st>>>(                                                 \
       static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
       static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
   if (nc <= 1) BS_ROWQ(1);
@@ -332,6 +354,18 @@ BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* ga
   BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
   return launch_row_quant<true>(y, residual, gamma, eps, q, scale, residual_out, M, K,
                                 static_cast<hipStream_t>(stream));
+}
+
+BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const void* gamma, float eps, void* q,
+                                      float* scale, void* residual_out, int M, int K, bs_stream_t stream) {
+  BS_CHECK(y && residual && gamma && q && scale && residual_out, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && K >= 128 && K % 128 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(y, 16) && bs_aligned(residual, 16) && bs_aligned(gamma, 16) && bs_aligned(q, 8) &&
+               bs_aligned(scale, 4) && bs_aligned(residual_out, 16),
+           BS_ERR_ALIGN);
+  BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
+  return launch_row_quant<true, true>(y, residual, gamma, eps, q, scale, residual_out, M, K,
+                                      static_cast<hipStream_t>(stream));
 }
 
 BS_API int silu_mul_quant_fp8(const void* gu, void* q, float* scale, int M, int N, bs_stream_t stream) {

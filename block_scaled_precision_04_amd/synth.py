@@ -22,6 +22,10 @@ not used):
   silu_chain        SiLU(gate) * up + per-token quant of the gate/up
                     projection's output [M, 2*17408], M in {8,4096},
                     feeding the W4A8 down projection (K=17408)
+  fp8_block_prefill block-FP8 W8A8 at large M: M in {2048, 8192} with the
+                    decode workload's (N,K) shapes and distributions; the
+                    group-scale chain: add + Gemma RMSNorm + per-128 quant at
+                    K=5120, M=4096, feeding block-FP8 with N=10240
 Seeds: 100 * workload index + case index.
 """
 import numpy as np
@@ -35,6 +39,8 @@ WORKLOADS = {
                          for m in (256, 2048, 8192)]),
     4: ("fused_chain", [(8, 17408, 5120), (4096, 17408, 5120)]),
     5: ("silu_chain", [(8, 17408), (4096, 17408)]),
+    6: ("fp8_block_prefill", [(m, n, k) for (n, k) in [(5120, 5120), (10240, 5120), (5120, 17408)]
+                              for m in (2048, 8192)] + [(4096, 10240, 5120)]),
 }
 
 
@@ -102,3 +108,10 @@ def silu_raw(case, M, N):
     """gate/up projection output gu bf16 [M, 2N]: N(0,1) with 0.1% outliers x8."""
     g = rng(seed_of(5, case))
     return bf16_normal(g, (M, 2 * N), 1.0, outlier_p=0.001, outlier_factor=8.0)
+
+
+def group_chain_raw(M, K):
+    """(y partial, residual, norm weight) of the group-scale chain: bf16 N(0,1),
+    N(0,1), N(0,0.1) (the fused chain's distributions)."""
+    g = rng(seed_of(6, 6) * 7 + 3)
+    return bf16_normal(g, (M, K), 1.0), bf16_normal(g, (M, K), 1.0), bf16_normal(g, (K,), 0.1)

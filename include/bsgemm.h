@@ -190,6 +190,19 @@ BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* ga
                              void* q, float* scale, void* residual_out, int M, int K,
                              bs_stream_t stream);
 
+/* The same producer for the block-FP8 consumer: one scale per token per
+ * 128-wide K group (the block-FP8 activation format of the radiance_kernels.py
+ * page, block_scaled_mm with per-token-per-128 activation scales) instead of
+ * one per token:
+ *   r, h as in add_rms_quant_fp8
+ *   scale[m, g] = max(max_{k in group g} |h| / 448, 1/(448*512))  (fp32)
+ *   q[m, k] = e4m3(clamp(h / scale[m, k/128], +-448))
+ * scale: fp32 [M, K/128] row-major.  K % 128 == 0, 128 <= K <= 32768; other
+ * arguments, aliasing and alignment as add_rms_quant_fp8. */
+BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const void* gamma, float eps,
+                                      void* q, float* scale, void* residual_out, int M, int K,
+                                      bs_stream_t stream);
+
 /* SiLU(gate) * up + per-token e4m3 quant (radiance_arnq.py page, the
  * silu_mul_quant op that replaces the MLP's SiluAndMul ahead of the down
  * projection; the quant is the per-token rule above):

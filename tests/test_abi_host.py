@@ -29,7 +29,7 @@ def blib():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     for name in ("bsgemm_fp8_block", "bsgemm_w4a8_mxfp4", "gemm_bf16_skinny", "add_rms_quant_fp8",
-                 "silu_mul_quant_fp8",
+                 "silu_mul_quant_fp8", "add_rms_quant_fp8_group128",
                  "bs_prelayout_fp8_block", "bs_prelayout_mxfp4", "bs_unprelayout_fp8_block",
                  "bs_unprelayout_mxfp4", "bs_workspace_bytes"):
         assert name in syms
@@ -59,6 +59,7 @@ def test_sizes(blib):
     assert blib.bs_prelayout_mxfp4_bytes(N, K) == off + (N // 16) * ((K // 128 + 3) // 4) * 256
     assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
     assert blib.bs_workspace_bytes(1, 8, 5120, 17408) > 0     # long K: split across workgroups
+    assert blib.bs_workspace_bytes(1, 2048, 5120, 17408) == 0  # large M: the tiled kernel, no split
     assert blib.bs_workspace_bytes(2, 8, 17408, 17408) > 0
     assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
     assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K
@@ -115,6 +116,8 @@ def test_skinny_and_producer_validation(blib):
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 65536, None) == -2
     assert blib.add_rms_quant_fp8(None, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5120, None) == -1
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, 8, 5120, None) == -7
+    assert blib.add_rms_quant_fp8_group128(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5000,
+                                           None) == -2                          # K % 128
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 17404, None) == -2       # N % 8
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 32776, None) == -2       # N above 32768
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 0, 17408, None) == -2       # no rows

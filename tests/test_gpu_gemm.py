@@ -88,24 +88,29 @@ def test_w4a8_prefill_workload_sampled(case):
     checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 prefill M={M} N={N} K={K}")
 
 
-def test_w4a8_fused_chain_consumer_on_gpu_producer_output():
-    """The fused chain: the GPU producer's own (q, scale) feeds the GPU GEMM;
-    the oracle GEMM is evaluated on those same bytes, isolating GEMM error."""
+def test_w4a8_fused_chain():
+    """The fused chain end to end: GPU producer -> GPU W4A8 GEMM against the
+    oracle producer -> oracle GEMM on the same raw draws (the oracle never
+    sees a GPU output)."""
+    from oracle import producer
     K, N = 5120, 17408
     wp, e = synth.mxfp4_weight_raw(4, 0, N, K)
     pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
     for case, M in ((0, 8), (1, 4096)):
         y, r, w = synth.producer_raw(case, M, K)
-        q, s, _ = bs.add_rms_quant_fp8(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
+        q, s, ro = bs.add_rms_quant_fp8(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
         c = bs.bsgemm_w4a8_mxfp4(q, s, desc, pre, ws=bs.alloc_workspace(bs.BS_OP_W4A8_MXFP4, M, N, K))
         torch.cuda.synchronize()
-        qh, sh, ch = q.cpu().numpy(), s.cpu().numpy(), host_bits16(c)
+        qo, so, ro_ref = producer.add_rms_quant(y, r, w, 1e-6)
+        checks.assert_producer_close(q.cpu().numpy(), s.cpu().numpy(), host_bits16(ro), qo, so, ro_ref,
+                                     f"chain producer M={M}")
+        ch = host_bits16(c)
         if M <= 8:
-            _, ce, asum = gemm.w4a8_mxfp4_gemm(qh, sh, wp, e)
+            _, ce, asum = gemm.w4a8_mxfp4_gemm(qo, so, wp, e)
             checks.assert_gemm_close(ch, ce, asum, "chain decode")
         else:
             rows, cols = sample_grid(M, N, 16, 32, seed=77)
-            _, ce, asum = gemm.w4a8_mxfp4_gemm_at(qh, sh, wp, e, rows, cols)
+            _, ce, asum = gemm.w4a8_mxfp4_gemm_at(qo, so, wp, e, rows, cols)
             checks.assert_gemm_close(ch[rows, cols], ce, asum, "chain prefill")
 
 
@@ -163,3 +168,65 @@ def test_skinny_edges(M, N, K):
     got = _skinny_run(x, w)
     _, ce, asum = gemm.bf16_gemm(x, w)
     checks.assert_gemm_close(got, ce, asum, f"skinny edge M={M} N={N} K={K}")
+
+
+# ------------------------------------------------------------------ block-FP8, large M (tiled kernel)
+FP8_PREFILL_CASES = [0, 1, 2, 4]     # M=2048 at the three (N,K) shapes, M=8192 at N=10240 K=5120
+
+
+@pytest.mark.parametrize("case", FP8_PREFILL_CASES)
+def test_fp8_block_prefill_workload_sampled(case):
+    M, N, K = synth.WORKLOADS[6][1][case]
+    assert bs.lib().bs_workspace_bytes(bs.BS_OP_FP8_BLOCK, M, N, K) == 0     # the tiled kernel needs none
+    aq, asc, wq, wsc = fp8_block_inputs(6, case, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc)
+    rows, cols = sample_grid(M, N, 24, 40, seed=100 + case)
+    _, ce, asum = gemm.fp8_block_gemm_at(aq, asc, wq, wsc, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, f"fp8 block prefill M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K,colmajor", [(512, 128, 128, False), (600, 384, 640, True), (1000, 1280, 1152, False),
+                                            (513, 256, 384, True), (777, 640, 2048, False)])
+def test_fp8_block_prefill_edges(M, N, K, colmajor):
+    """Tiled kernel at ragged M (row tails inside a 256-row tile), N = 1.5 and
+    2.5 tiles (a half tile of idle waves), a single K step, and activation
+    scales read through column-major strides; full oracle."""
+    aq, asc, wq, wsc = fp8_block_inputs(9, 7 * M + N, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc, col_major_scale=colmajor)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(got, ce, asum, f"fp8 block prefill edge M={M} N={N} K={K}")
+
+
+def test_fp8_block_prefill_no_out_of_bounds_writes_and_ldc():
+    M, N, K = 700, 384, 512
+    aq, asc, wq, wsc = fp8_block_inputs(9, 11, M, N, K)
+    pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+    big = torch.full((M + 2, N + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[1:M + 1, 8:8 + N]
+    bs.bsgemm_fp8_block(dev_u8(aq), dev_f32(asc), desc, pre, dev_f32(wsc), out=view)
+    torch.cuda.synchronize()
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[1:M + 1, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "fp8 prefill strided out")
+
+
+def test_fp8_block_group_chain():
+    """The group-scale chain end to end: GPU producer -> GPU block-FP8 GEMM
+    against oracle producer -> oracle GEMM on the same raw draws."""
+    from oracle import producer, quant
+    M, N, K = synth.WORKLOADS[6][1][6]
+    y, r, w = synth.group_chain_raw(M, K)
+    wbits = synth.fp8_block_raw(6, 6, 1, N, K)[1]
+    wq, wsc = quant.quant_block128_bf16(wbits)
+    pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+    q, s, ro = bs.add_rms_quant_fp8_group128(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
+    c = bs.bsgemm_fp8_block(q, s, desc, pre, dev_f32(wsc))
+    torch.cuda.synchronize()
+    qo, so, ro_ref = producer.add_rms_quant_group128(y, r, w, 1e-6)
+    checks.assert_producer_close(q.cpu().numpy(), s.cpu().numpy(), host_bits16(ro), qo, so, ro_ref, "group chain")
+    rows, cols = sample_grid(M, N, 16, 32, seed=78)
+    _, ce, asum = gemm.fp8_block_gemm_at(qo, so, wq, wsc, rows, cols)
+    checks.assert_gemm_close(host_bits16(c)[rows, cols], ce, asum, "group chain GEMM")

@@ -124,3 +124,19 @@ def test_silu_mul_quant_special_rows(M):
     checks.assert_codes_close(qg, sg, qo, so, f"silu special rows M={M}")
     assert np.all((qg[0] & 0x7F) == 0) and np.float32(sg[0]) == np.float32(1.0 / (448 * 512))
     assert qg[3, 17] == 0x7E and np.all((np.delete(qg[3], 17) & 0x7F) == 0)
+
+
+# ----------------------------------------------------------------- group-scale norm producer
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 2048), (5, 5120), (2, 32768), (300, 640)])
+def test_group_producer_shapes(M, K):
+    g = synth.rng(800 + K)
+    y = synth.bf16_normal(g, (M, K), 1.0)
+    r = synth.bf16_normal(g, (M, K), 1.0)
+    w = synth.bf16_normal(g, (K,), 0.1)
+    y[0, :128] = synth.bf16_normal(g, (128,), 1e-3)        # a quiet first group
+    q, s, ro = bs.add_rms_quant_fp8_group128(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
+    torch.cuda.synchronize()
+    qo, so, roo = producer.add_rms_quant_group128(y, r, w, 1e-6)
+    assert s.shape == (M, K // 128)
+    checks.assert_producer_close(host_u8(q), s.cpu().numpy(), host_bits16(ro), qo, so, roo,
+                                 f"group producer M={M} K={K}")
