@@ -142,10 +142,13 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
  * c:       bf16 [M, N], leading dimension ldc (elements, multiple of 4).
  * ws:      bs_workspace_bytes(BS_OP_FP8_BLOCK, M, N, K) bytes (256-byte
  *          aligned, zeroed once) when that is non-zero: K split across
- *          workgroups; otherwise may be NULL.  M > 64 runs as consecutive
- *          64-row launches on the stream, all sharing ws.
- * Needs M >= 1, N % 128 == 0, K % 128 == 0, lda < 2^25; a, c and w_pre
- * 16-byte aligned. */
+ *          workgroups; otherwise may be NULL.
+ * Regimes: M < 512 streams the weight (small M; 64 < M < 512 runs as
+ * consecutive 64-row launches on the stream, all sharing ws); M >= 512 runs
+ * the LDS-tiled kernel (256x256 tiles), which needs no workspace.
+ * Needs M >= 1, N % 128 == 0, K % 128 == 0, K < 2^24, lda < 2^25,
+ * 0 <= as_stride_m < 2^22, as_stride_g >= 0; a, c and w_pre 16-byte aligned,
+ * the scales 4-byte aligned. */
 BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, int64_t as_stride_m,
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre,
                             const float* w_scale, void* c, int64_t ldc, int M, int N, int K,
