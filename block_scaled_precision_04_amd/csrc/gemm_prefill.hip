@@ -32,6 +32,7 @@
 // m-tiles sweep the n-tiles together), so the workgroups resident on one XCD
 // at any moment share a few activation and weight tiles in that XCD's L2.
 #include <algorithm>
+#include <numeric>
 
 #include "common.h"
 
@@ -405,32 +406,48 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
   return bs_launch_status();
 }
 
-// Tile and K-split choice.  256x256 tiles (one workgroup per CU) when the
-// grid has at least 384 of them (1.5 rounds of 256 CUs: fewer leave a costly
-// partial round, e.g. 320 tiles run 20% slower than 1280 128x128 tiles);
-// otherwise 128x128 (two per CU), and when even those leave most of the 512
-// workgroup slots empty, K is split so that about 512 workgroups run,
-// keeping at least 8 K steps (1024 K) per split.
+// Tile and K-split choice.  256x256 tiles run one workgroup per CU, so a
+// grid of T big tiles takes ceil(T / 256) rounds and a partial last round
+// costs nearly a whole one (1088 tiles: 335 us against 4 x 67 us).  When
+// there are at least 256 big tiles, the big-tile launch takes the widest
+// column range [0, n_main) whose tile count is a whole number of rounds --
+// n_main / 256 a multiple of 256 / gcd(m_tiles, 256) -- and the remaining
+// column strip (less than one round of big tiles) runs as 128x128 tiles,
+// two workgroups per CU.  Small-tile grids that leave most of the 512
+// workgroup slots empty split K so that about 512 workgroups run, keeping
+// at least 8 K steps (1024 K) per split.  Below 256 big tiles everything
+// runs as small tiles (that way 320 tiles ran 20% faster than as big ones).
 struct PrefillPlan {
-  bool big;
-  int s, tiles;
+  int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
+  int s;        // K splits of the small-tile launch over columns [n_main, N)
+  int tiles;    // small tiles (0: none)
 };
 PrefillPlan prefill_plan(int M, int N, int K) {
   const int KS = K / 128;
-  const int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 384) return {true, 1, big_tiles};
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int s = 1;
-  if (tiles < 384) s = std::max(1, std::min(512 / tiles, KS / 8));
-  s = std::min(s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
-  return {false, s, tiles};
+  const int mt = (M + 255) / 256, nt = (N + 255) / 256;
+  PrefillPlan p{0, 1, 0};
+  if (mt * nt >= 256) {
+    p.n_main = N;
+    if ((mt * nt) % 256 != 0) {
+      const int g = 256 / std::gcd(mt, 256);   // n-tile multiple that fills whole rounds
+      const int n1 = (nt - 1) / g * g;
+      if (n1 >= 1 && mt * (nt - n1) < 256) p.n_main = n1 * 256;
+    }
+  }
+  const int ns = N - p.n_main;
+  if (ns > 0) {
+    p.tiles = ((M + 127) / 128) * ((ns + 127) / 128);
+    if (p.tiles < 384) p.s = std::max(1, std::min(512 / p.tiles, KS / 8));
+    p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
+  }
+  return p;
 }
 
 }  // namespace
 
 size_t bs_prefill_workspace(int M, int N, int K) {
   const PrefillPlan pl = prefill_plan(M, N, K);
-  if (pl.s <= 1) return 0;
+  if (pl.tiles == 0 || pl.s <= 1) return 0;
   return static_cast<size_t>(pl.s) * pl.tiles * 128 * 128 * sizeof(float) + static_cast<size_t>(pl.tiles) * sizeof(int);
 }
 
@@ -439,6 +456,16 @@ int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const
   const int KS = K / 128;
   const uint8_t* sc = reinterpret_cast<const uint8_t*>(wsc);
   const PrefillPlan pl = prefill_plan(M, N, K);
-  if (pl.big) return launch_cfg<256, 256, 2, 2, 1, false, true>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, 1, nullptr, st);
-  return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w, sc, c, ldc, M, N, KS, 4, pl.s, ws, st);
+  if (pl.n_main > 0) {
+    const int rc = launch_cfg<256, 256, 2, 2, 1, false, true>(a, lda, as, w, sc, c, ldc, M, pl.n_main, KS, 4, 1,
+                                                               nullptr, st);
+    if (rc != BS_OK || pl.tiles == 0) return rc;
+  }
+  // the column strip: the weight's n-tiles from n_main / 16 on (codes KS KiB
+  // and scales ceil(KS/4) * 256 bytes per 16-column tile), output columns
+  // from n_main on
+  const size_t nt_off = static_cast<size_t>(pl.n_main) / 16;
+  return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w + nt_off * KS * 1024,
+                                                    sc + nt_off * ((KS + 3) / 4) * 256, c + pl.n_main, ldc, M,
+                                                    N - pl.n_main, KS, 4, pl.s, ws, st);
 }
