@@ -230,3 +230,20 @@ def test_fp8_block_group_chain():
     rows, cols = sample_grid(M, N, 16, 32, seed=78)
     _, ce, asum = gemm.fp8_block_gemm_at(qo, so, wq, wsc, rows, cols)
     checks.assert_gemm_close(host_bits16(c)[rows, cols], ce, asum, "group chain GEMM")
+
+
+def test_w4a8_prefill_column_strip():
+    """A grid of 264 large tiles (8 x 33): the large-tile launch takes the
+    first 8192 columns (256 tiles, one round) and a 48-column strip runs as
+    split small tiles with offset weight, scale and output pointers.  The
+    check covers both parts and the seam between them."""
+    M, N, K = 2048, 8240, 1024
+    aq, asc, wp, e = w4a8_inputs(8, 5, M, N, K)
+    got = host_bits16(_w4_run(aq, asc, wp, e))
+    rows, cols = sample_grid(M, N, 16, 24, seed=5)
+    seam = np.array([8176, 8191, 8192, 8193, 8207, 8208, 8223, 8224, 8239])
+    rr, cc = np.meshgrid(np.unique(rows), seam, indexing="ij")
+    rows = np.r_[rows, rr.reshape(-1)]
+    cols = np.r_[cols, cc.reshape(-1)]
+    _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 column strip")
