@@ -72,6 +72,7 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre, const float* w_scale,
                             void* c, int64_t ldc, int M, int N, int K, void* ws, size_t ws_bytes,
                             bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(a && a_scale && wd && w_pre && w_scale && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= kFp8MaxM && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_FP8_BLOCK && wd->N == N && wd->K == K,
@@ -99,6 +100,7 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
 BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, const bs_wdesc* wd,
                              const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
                              size_t ws_bytes, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(a && a_scale && wd && w_pre && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= (1 << 22) && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_MXFP4 && wd->N == N && wd->K == K &&
@@ -126,6 +128,7 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
 
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws, size_t ws_bytes,
                             bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(x && w && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= kSkinnyMaxM && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(w, 16) && bs_aligned(c, 4), BS_ERR_ALIGN);

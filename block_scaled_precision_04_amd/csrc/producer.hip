@@ -346,6 +346,7 @@ extern "C" {
 
 BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* gamma, float eps, void* q,
                              float* scale, void* residual_out, int M, int K, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(y && residual && gamma && q && scale && residual_out, BS_ERR_NULL);
   BS_CHECK(M >= 1 && K >= 8 && K % 8 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(y, 16) && bs_aligned(residual, 16) && bs_aligned(gamma, 16) && bs_aligned(q, 8) &&
@@ -358,6 +359,7 @@ BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* ga
 
 BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const void* gamma, float eps, void* q,
                                       float* scale, void* residual_out, int M, int K, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(y && residual && gamma && q && scale && residual_out, BS_ERR_NULL);
   BS_CHECK(M >= 1 && K >= 128 && K % 128 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(y, 16) && bs_aligned(residual, 16) && bs_aligned(gamma, 16) && bs_aligned(q, 8) &&
@@ -369,6 +371,7 @@ BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const
 }
 
 BS_API int silu_mul_quant_fp8(const void* gu, void* q, float* scale, int M, int N, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(gu && q && scale, BS_ERR_NULL);
   BS_CHECK(M >= 1 && N >= 8 && N % 8 == 0 && N <= kMaxRowK, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(gu, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);
@@ -376,6 +379,7 @@ BS_API int silu_mul_quant_fp8(const void* gu, void* q, float* scale, int M, int 
 }
 
 BS_API int quant_fp8_per_token(const void* x, void* q, float* scale, int M, int K, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(x && q && scale, BS_ERR_NULL);
   BS_CHECK(M >= 1 && K >= 8 && K % 8 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);
@@ -384,6 +388,7 @@ BS_API int quant_fp8_per_token(const void* x, void* q, float* scale, int M, int 
 }
 
 BS_API int quant_fp8_group128(const void* x, void* q, float* scale, int M, int K, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(x && q && scale, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= 65535 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(q, 8) && bs_aligned(scale, 4), BS_ERR_ALIGN);

@@ -8,6 +8,9 @@
  * Arguments are validated on the host before anything is launched: on a
  * failed check the call returns a negative status and enqueues nothing.  A
  * launch failure returns BS_ERR_LAUNCH.  No C++ exception crosses this ABI.
+ * A call with zero rows (M == 0 for the GEMMs, producers and activation
+ * quantizers) is an empty batch: it returns BS_OK before reading any other
+ * argument (pointers may be NULL) and launches nothing.
  * The library keeps no state between calls and is safe to call from several
  * host threads.
  *

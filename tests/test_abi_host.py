@@ -83,8 +83,9 @@ def test_gemm_argument_validation(blib):
     assert fp8(a=None) == -1
     assert fp8(N=200) == -2
     assert fp8(K=500) == -2
-    assert fp8(M=0) == -2
-    assert fp8(N=384) == -4                        # descriptor says N=256
+    assert fp8(M=0) == 0                           # empty batch
+    assert fp8(M=-1) == -2
+    assert fp8(N=384) == -4                       # descriptor says N=256
     bad = WDesc(0, BS_LAYOUT_FP8_BLOCK, 256, 512, 0, 0, 0, 0)
     assert fp8(desc=bad) == -4
     assert fp8(lda=500) == -3
@@ -120,7 +121,7 @@ def test_skinny_and_producer_validation(blib):
                                            None) == -2                          # K % 128
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 17404, None) == -2       # N % 8
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 32776, None) == -2       # N above 32768
-    assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 0, 17408, None) == -2       # no rows
+    assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 0, 17408, None) == 0        # no rows: empty batch
     assert blib.silu_mul_quant_fp8(None, FAKE, FAKE, 8, 17408, None) == -1
     assert blib.silu_mul_quant_fp8(ctypes.c_void_p(0x10008), FAKE, FAKE, 8, 17408, None) == -3
     assert blib.quant_fp8_group128(FAKE, FAKE, FAKE, 8, 5000, None) == -2
@@ -134,3 +135,18 @@ def test_prelayout_validation(blib):
     assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 100, 256, 512, ctypes.byref(d), None) == -7   # out too small
     assert blib.bs_prelayout_mxfp4(FAKE, FAKE, FAKE, 1 << 20, 32, 100, ctypes.byref(d), None) == -2
     assert blib.bs_unprelayout_fp8_block(ctypes.byref(d), FAKE, FAKE, None) == -4             # empty descriptor
+
+
+def test_empty_batch_is_a_no_op(blib):
+    """M == 0: BS_OK before any other argument is read (NULL pointers, no
+    descriptor) and nothing is launched (no stream is touched)."""
+    assert blib.bsgemm_fp8_block(None, 0, None, 0, 0, None, None, None, None, 0, 0, 256, 512, None, 0, None) == 0
+    assert blib.bsgemm_w4a8_mxfp4(None, 0, None, None, None, None, 0, 0, 256, 512, None, 0, None) == 0
+    assert blib.gemm_bf16_skinny(None, None, None, 0, 96, 5120, None, 0, None) == 0
+    assert blib.add_rms_quant_fp8(None, None, None, ctypes.c_float(1e-6), None, None, None, 0, 5120, None) == 0
+    assert blib.add_rms_quant_fp8_group128(None, None, None, ctypes.c_float(1e-6), None, None, None, 0, 5120,
+                                           None) == 0
+    assert blib.silu_mul_quant_fp8(None, None, None, 0, 17408, None) == 0
+    assert blib.quant_fp8_per_token(None, None, None, 0, 5120, None) == 0
+    assert blib.quant_fp8_group128(None, None, None, 0, 5120, None) == 0
+    assert blib.bs_workspace_bytes(1, 0, 256, 512) == 0

@@ -247,3 +247,29 @@ def test_w4a8_prefill_column_strip():
     cols = np.r_[cols, cc.reshape(-1)]
     _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
     checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 column strip")
+
+
+def test_empty_batch_through_the_binding():
+    """Zero-row inputs (torch may hand out NULL data pointers for them) give
+    empty outputs and no error, for every GEMM and producer."""
+    K, N = 512, 256
+    wq = np.zeros((N, K), np.uint8)
+    pre8, d8 = bs.prelayout_fp8_block(dev_u8(wq))
+    c = bs.bsgemm_fp8_block(torch.empty((0, K), dtype=torch.uint8, device="cuda"),
+                            torch.empty((0, K // 128), device="cuda"), d8, pre8,
+                            torch.ones((N // 128, K // 128), device="cuda"))
+    assert c.shape == (0, N)
+    pre4, d4 = bs.prelayout_mxfp4(dev_u8(np.zeros((N, K // 2), np.uint8)), dev_u8(np.full((N, K // 32), 127, np.uint8)))
+    c = bs.bsgemm_w4a8_mxfp4(torch.empty((0, K), dtype=torch.uint8, device="cuda"), torch.empty((0,), device="cuda"),
+                             d4, pre4)
+    assert c.shape == (0, N)
+    x = torch.empty((0, 5120), dtype=torch.bfloat16, device="cuda")
+    assert bs.gemm_bf16_skinny(x, torch.zeros((96, 5120), dtype=torch.bfloat16, device="cuda")).shape == (0, 96)
+    g = torch.zeros((5120,), dtype=torch.bfloat16, device="cuda")
+    q, s, r = bs.add_rms_quant_fp8(x, x, g)
+    assert q.shape == (0, 5120) and s.shape == (0,) and r.shape == (0, 5120)
+    q, s, r = bs.add_rms_quant_fp8_group128(x, x, g)
+    assert s.shape == (0, 40)
+    q, s = bs.silu_mul_quant_fp8(torch.empty((0, 2 * 17408), dtype=torch.bfloat16, device="cuda"))
+    assert q.shape == (0, 17408)
+    torch.cuda.synchronize()
