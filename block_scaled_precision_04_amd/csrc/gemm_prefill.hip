@@ -13,18 +13,20 @@
 // Tiling: a workgroup computes a BM x BN output tile with WM x WN waves; each
 // wave owns (BM/WM) x (BN/WN) as 32x32 MFMA sub-tiles with fp32 accumulators
 // (the large tiles keep them in the accumulator registers).  K advances in
-// 128-wide steps.  Each step's activation tile (BM rows x 128 bytes) and
-// weight tile (BN/16 fragment-order 1 KiB blocks, copied as they are) are
-// moved global -> LDS by the direct-to-LDS 16-byte load (no register
-// staging), double buffered: the loads of step k+1 are in flight while step
-// k is computed.  Activation rows are stored without padding; their eight
-// 16-byte chunks are XOR-swizzled by the row index so that the fragment reads
-// (32 rows, same chunk) spread over the LDS banks.  The e8m0 scales are read
-// straight from the pre-laid-out scale section (one dword per lane per four
-// steps).  The per-token activation scale multiplies the accumulator in the
+// 128-wide steps.  Each step's activation tile (BM rows x 128 bytes), weight
+// tile (BN/16 fragment-order 1 KiB blocks, copied as they are) and the e8m0
+// dwords of the tile's 16-column blocks (one dword per lane per four steps,
+// as pre-laid-out) are moved global -> LDS by the direct-to-LDS 16-byte load
+// (no register staging) into one of three stage buffers: the loads of step
+// k+2 are issued while step k is computed.  Activation rows are stored
+// without padding; their eight 16-byte chunks are XOR-swizzled by the row
+// index so that the fragment reads (32 rows, same chunk) spread over the LDS
+// banks.  The per-token activation scale multiplies the accumulator in the
 // epilogue, then bf16 RNE and store.  The first MFMA operand is the weight
 // (rows = n), the second the activation (rows = m), so each lane stores four
-// consecutive n of one m (8 bytes).
+// consecutive n of one m (8 bytes).  Which tile size runs where (and the
+// column strip that avoids a partial last round of large tiles) is decided by
+// prefill_plan below.
 //
 // Workgroup -> tile order: gfx950 hands workgroup b to XCD b % 8, and each
 // XCD has its own L2.  The tile sequence is cut into eight contiguous chunks,
@@ -413,9 +415,10 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
 // column range [0, n_main) whose tile count is a whole number of rounds --
 // n_main / 256 a multiple of 256 / gcd(m_tiles, 256) -- and the remaining
 // column strip (less than one round of big tiles) runs as 128x128 tiles,
-// two workgroups per CU.  Small-tile grids that leave most of the 512
-// workgroup slots empty split K so that about 512 workgroups run, keeping
-// at least 8 K steps (1024 K) per split.  Below 256 big tiles everything
+// two workgroups per CU.  Small-tile grids under 256 tiles split K so that
+// about 512 workgroups run, keeping at least 8 K steps (1024 K) per split
+// (measured: 80 and 160 tiles gain from 6 and 3 splits; 256 tiles, such as
+// the column strips, run faster unsplit).  Below 256 big tiles everything
 // runs as small tiles (that way 320 tiles ran 20% faster than as big ones).
 struct PrefillPlan {
   int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
@@ -437,7 +440,7 @@ PrefillPlan prefill_plan(int M, int N, int K) {
   const int ns = N - p.n_main;
   if (ns > 0) {
     p.tiles = ((M + 127) / 128) * ((ns + 127) / 128);
-    if (p.tiles < 384) p.s = std::max(1, std::min(512 / p.tiles, KS / 8));
+    if (p.tiles < 256) p.s = std::max(1, std::min(512 / p.tiles, KS / 8));
     p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
   }
   return p;
