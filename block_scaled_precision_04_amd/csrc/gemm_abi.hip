@@ -84,12 +84,16 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
            BS_ERR_ALIGN);
   BS_CHECK(as_stride_m >= 0 && as_stride_g >= 0, BS_ERR_ARG);
   BS_CHECK(K < (1 << 24), BS_ERR_SHAPE);  // weight tiles are addressed with 32-bit offsets
-  // the tiled kernel addresses a tile's activation scales with 32-bit offsets
+  // the tiled kernel addresses a tile's activation rows (256 * lda), activation
+  // scales (256 * as_stride_m floats) and weight scales ((N/128) * (K/128)
+  // floats) with unsigned 32-bit offsets
   BS_CHECK(as_stride_m < (1 << 22), BS_ERR_SHAPE);
-  if (M >= bs_fp8_prefill_min_m())
+  if (M >= bs_fp8_prefill_min_m()) {
+    BS_CHECK(lda < (1 << 24) && static_cast<uint64_t>(N / 128) * (K / 128) < (1ull << 30), BS_ERR_SHAPE);
     return bs_launch_fp8_block_prefill(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,
                                        static_cast<const uint8_t*>(w_pre), w_scale, static_cast<uint16_t*>(c), ldc,
                                        M, N, K, static_cast<hipStream_t>(stream));
+  }
   const int wst = check_workspace(bs_decode_workspace(M, N, K, false), ws, ws_bytes);
   if (wst != BS_OK) return wst;
   return bs_launch_fp8_block_decode(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,
@@ -109,8 +113,10 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
            BS_ERR_ALIGN);
-  // both kernels address the activation with 32-bit offsets
+  // both kernels address the activation, and the tiled kernel the weight
+  // codes (N * K / 2 bytes), with unsigned 32-bit offsets
   BS_CHECK(static_cast<uint64_t>(M) * static_cast<uint64_t>(lda) < (1ull << 32) && lda < (1 << 25), BS_ERR_SHAPE);
+  BS_CHECK(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) / 2 < (1ull << 32), BS_ERR_SHAPE);
   const uint8_t* w = static_cast<const uint8_t*>(w_pre);
   const uint32_t* wsc = reinterpret_cast<const uint32_t*>(w + wd->scales_offset);
   hipStream_t st = static_cast<hipStream_t>(stream);

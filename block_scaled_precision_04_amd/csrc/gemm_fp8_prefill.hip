@@ -82,8 +82,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
   const int nt0 = n0 >> 4;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  // ---- direct-to-LDS sources: 64-bit tile bases, 32-bit per-lane offsets
-  // within the tile (< 256 * lda and < 16 * KS * 2 KiB).  A load instruction
+  // ---- direct-to-LDS sources: 64-bit tile bases, unsigned 32-bit per-lane
+  // offsets within the tile (< 256 * lda and < 16 * KS * 2 KiB; the host
+  // keeps both below 2^32).  A load instruction
   // writes lane i's 16 bytes at (uniform LDS base) + 16*i, so each lane
   // fetches the chunk that belongs at its LDS position.  Rows past M and
   // 16-column tiles past N fetch the last valid row / tile (finite data,
@@ -95,7 +96,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
   for (int i = 0; i < kAIters; ++i) {
     const int p = (i * kWaves + wave) * 64 + l;      // 16-byte position in the activation stage
     const int row = p >> 3, slot = p & 7;
-    aoff[i] = static_cast<uint32_t>((min(m0 + row, M - 1) - m0) * lda + 16 * swz(row, slot));
+    aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1) - m0) * static_cast<uint32_t>(lda) +
+              static_cast<uint32_t>(16 * swz(row, slot));
   }
   // weight stage: 1 KiB half-blocks h = 2 * (16-column tile) + half, in the
   // pre-laid-out order (lane-major 16-byte chunks)
@@ -104,14 +106,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
   for (int j = 0; j < kBIters; ++j) {
     const int h = j * kWaves + wave;
     const int ntl = min(nt0 + (h >> 1), NT - 1) - nt0;
-    boff[j] = static_cast<uint32_t>(ntl * KS * 2048 + (h & 1) * 1024 + l * 16);
+    boff[j] = static_cast<uint32_t>(ntl) * static_cast<uint32_t>(KS) * 2048u + static_cast<uint32_t>((h & 1) * 1024 + l * 16);
   }
   // activation scales: wave w < kSWaves loads rows 64w .. 64w+63 of the tile
   // (tile base + K-step offset are 64-bit scalars; the row offset < 256 * as_m)
   const float* as_tile = as + static_cast<int64_t>(m0) * as_m;
   const uint32_t soff = static_cast<uint32_t>((min(m0 + wave * 64 + l, M - 1) - m0) * as_m * 4);
   // weight scales of the tile's 128-column blocks: lane j -> block (n0/128 + j)
-  const uint32_t woff = static_cast<uint32_t>(min((n0 >> 7) + l, (N >> 7) - 1) * KS * 4);
+  const uint32_t woff = static_cast<uint32_t>(min((n0 >> 7) + l, (N >> 7) - 1)) * static_cast<uint32_t>(KS) * 4u;
   auto dma_stage = [&](int ks, int buf) {
     const uint32_t base = lds0 + buf * kStage;
 #pragma unroll

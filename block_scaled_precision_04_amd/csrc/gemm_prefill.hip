@@ -105,20 +105,21 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   for (int i = 0; i < C::kAIters; ++i) {
     const int p = (i * C::kWaves + wave) * 64 + l;  // 16-byte position in the activation stage
     const int row = p >> 3, slot = p & 7;
-    aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1) * lda + 16 * swz(row, slot));
+    aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(lda) +
+              static_cast<uint32_t>(16 * swz(row, slot));
   }
   uint32_t boff_g[C::kBIters];
 #pragma unroll
   for (int i = 0; i < C::kBIters; ++i) {
     const int nt = min(nt0 + i * C::kWaves + wave, NT - 1);
-    boff_g[i] = static_cast<uint32_t>(nt * KS * 1024 + l * 16);
+    boff_g[i] = static_cast<uint32_t>(nt) * static_cast<uint32_t>(KS) * 1024u + static_cast<uint32_t>(l * 16);
   }
   uint32_t soff_g[C::kSIters];
 #pragma unroll
   for (int i = 0; i < C::kSIters; ++i) {
     const int p = (i * C::kWaves + wave) * 64 + l;
     const int nt = min(nt0 + (p >> 4), NT - 1);
-    soff_g[i] = static_cast<uint32_t>(nt * KQ * 256 + (p & 15) * 16);
+    soff_g[i] = static_cast<uint32_t>(nt) * static_cast<uint32_t>(KQ) * 256u + static_cast<uint32_t>((p & 15) * 16);
   }
   // the i-th direct-to-LDS load of step ks (i < kDmaAll) into buffer buf
   auto dma_one = [&](int i, int ks, int buf) {

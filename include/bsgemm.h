@@ -150,8 +150,9 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
  * consecutive 64-row launches on the stream, all sharing ws); M >= 512 runs
  * the LDS-tiled kernel (256x256 tiles), which needs no workspace.
  * Needs M >= 1, N % 128 == 0, K % 128 == 0, K < 2^24, lda < 2^25,
- * 0 <= as_stride_m < 2^22, as_stride_g >= 0; a, c and w_pre 16-byte aligned,
- * the scales 4-byte aligned. */
+ * 0 <= as_stride_m < 2^22, as_stride_g >= 0 (and, for M >= 512, lda < 2^24
+ * and (N/128)*(K/128) < 2^30); a, c and w_pre 16-byte aligned, the scales
+ * 4-byte aligned. */
 BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, int64_t as_stride_m,
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre,
                             const float* w_scale, void* c, int64_t ldc, int M, int N, int K,
@@ -163,11 +164,14 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
  * a: e4m3 [M, K] (lda bytes, multiple of 16); a_scale: fp32 [M];
  * w_pre: pre-laid-out by bs_prelayout_mxfp4 (desc wd); c: bf16 [M, N] (ldc
  * elements, multiple of 4).  Needs M >= 1, N % 16 == 0, K % 128 == 0.
- * Small M (<= 64) streams the weight (bandwidth-bound) and, when K is split
- * across workgroups, needs ws of bs_workspace_bytes(BS_OP_W4A8_MXFP4, M, N, K)
- * bytes (256-byte aligned, zeroed once); large M runs the LDS-tiled
- * scaled-MFMA kernel (compute-bound) and needs no workspace.
- * Needs M * lda < 2^32 and lda < 2^25 (32-bit activation offsets). */
+ * Small M (<= 64) streams the weight (bandwidth-bound); large M runs the
+ * LDS-tiled scaled-MFMA kernel (compute-bound; a grid whose large tiles end
+ * in a partial round runs its last columns as small tiles).  Whenever either
+ * splits K across workgroups (small grids, column strips) the call needs ws
+ * of bs_workspace_bytes(BS_OP_W4A8_MXFP4, M, N, K) bytes (256-byte aligned,
+ * zeroed once); when that is 0, ws may be NULL.
+ * Needs M * lda < 2^32, lda < 2^25 and N * K / 2 < 2^32 (32-bit activation
+ * and weight offsets). */
 BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, const bs_wdesc* wd,
                              const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
                              size_t ws_bytes, bs_stream_t stream);

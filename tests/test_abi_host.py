@@ -137,6 +137,20 @@ def test_prelayout_validation(blib):
     assert blib.bs_unprelayout_fp8_block(ctypes.byref(d), FAKE, FAKE, None) == -4             # empty descriptor
 
 
+def test_offset_range_limits(blib):
+    """Shapes whose 32-bit in-kernel offsets would overflow are refused on the
+    host: block-FP8 tiled path lda < 2^24, W4A8 N*K/2 < 2^32."""
+    from block_scaled_precision_04_amd._binding import WDesc, BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, BS_LAYOUT_MXFP4
+    d = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 512, 256 * 512, 0, 0, 256 * 512)
+    big_lda = 1 << 24
+    assert blib.bsgemm_fp8_block(FAKE, big_lda, FAKE, 4, 1, ctypes.byref(d), FAKE, FAKE, FAKE, 256, 1024, 256, 512,
+                                 None, 0, None) == -2       # tiled path (M >= 512)
+    N, K = 65536, 131072
+    dm = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, N, K, N * K // 2, N * K // 2, N * K // 32, N * K // 2 + N * K // 32)
+    assert blib.bsgemm_w4a8_mxfp4(FAKE, K, FAKE, ctypes.byref(dm), ctypes.c_void_p(0x100000), FAKE, N, 8, N, K,
+                                  None, 0, None) == -2
+
+
 def test_empty_batch_is_a_no_op(blib):
     """M == 0: BS_OK before any other argument is read (NULL pointers, no
     descriptor) and nothing is launched (no stream is touched)."""
