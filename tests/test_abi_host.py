@@ -164,3 +164,44 @@ def test_empty_batch_is_a_no_op(blib):
     assert blib.quant_fp8_per_token(None, None, None, 0, 5120, None) == 0
     assert blib.quant_fp8_group128(None, None, None, 0, 5120, None) == 0
     assert blib.bs_workspace_bytes(1, 0, 256, 512) == 0
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "bsgemm.h"
+
+int main(void) {
+  bs_wdesc d;
+  memset(&d, 0, sizeof d);
+  if (bs_version() < 100) return 1;
+  if (strcmp(bs_status_string(BS_OK), "ok") != 0) return 2;
+  if (bs_prelayout_fp8_block_bytes(256, 512) != (size_t)256 * 512) return 3;
+  if (bs_workspace_bytes(BS_OP_FP8_BLOCK, 8, 5120, 17408) == 0) return 4;
+  /* host-side validation only: nothing below reaches a device */
+  if (bsgemm_fp8_block(NULL, 512, NULL, 4, 1, &d, NULL, NULL, NULL, 256, 8, 256, 512, NULL, 0, NULL)
+      != BS_ERR_NULL) return 5;
+  if (bsgemm_w4a8_mxfp4(NULL, 0, NULL, NULL, NULL, NULL, 0, 0, 256, 512, NULL, 0, NULL) != BS_OK) return 6;
+  if (add_rms_quant_fp8(NULL, NULL, NULL, 1e-6f, NULL, NULL, NULL, 8, 5121, NULL) != BS_ERR_NULL) return 7;
+  printf("c client ok\n");
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_links(tmp_path, blib):
+    """A C99 program that includes only bsgemm.h compiles with -Wall -Werror,
+    links against the library and sees the documented host-side behaviour."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(LIB)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-L", libdir, "-lbsgemm", "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    assert out.strip() == "c client ok"
