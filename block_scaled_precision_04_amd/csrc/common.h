@@ -125,5 +125,35 @@ BS_INLINE void xcd_tile(int b, int m_tiles, int n_tiles, int group_m, int& mt, i
   nt = loc / gsize;
 }
 
+// Split-K reduction of the last-arriving workgroup: sum[v] = the S fp32
+// partials base[b * stride + v * VSTRIDE] added in split order b = 0, 1, ...
+// (deterministic).  The partials were written with device-scope stores, so
+// they are read with device-scope loads, which are served past the XCD's L2:
+// a round trip costs about a microsecond.  The loads of U splits are all
+// issued before any of them is added, so the reduction waits ceil(S / U)
+// round trips rather than one per split and value group.  Splits past S
+// re-read split S - 1 (valid memory) and are not added.
+template <int NV, int VSTRIDE, int U>
+BS_INLINE void sum_partials(float (&sum)[NV], const float* base, size_t stride, int S) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) sum[v] = 0.0f;
+  for (int b0 = 0; b0 < S; b0 += U) {
+    float x[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* src = base + static_cast<size_t>(min(b0 + u, S - 1)) * stride;
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        x[u][v] = __hip_atomic_load(src + v * VSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = b0 + u < S;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) sum[v] = live ? sum[v] + x[u][v] : sum[v];
+    }
+  }
+}
+
 constexpr float kFp8Max = 448.0f;
 constexpr double kMinScale = 1.0 / (448.0 * 512.0);

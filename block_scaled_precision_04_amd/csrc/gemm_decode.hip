@@ -313,17 +313,18 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
     last = __hip_atomic_fetch_add(&p.counters[cidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!last || !owner) return;
+  // value (t, mb, j) of split b sits at frag(b, t, mb) + 64 j = frag(0, 0, 0) + b * split stride + 64 v
+  constexpr int kNV = T * MB * 4;
+  constexpr int kU = kNV >= 32 ? 2 : (kNV >= 16 ? 4 : 8);
+  float tot[kNV];
+  sum_partials<kNV, 64, kU>(tot, frag(0, 0, 0),
+                            static_cast<size_t>(gridDim.z) * gridDim.x * (TW * T * MB * 256), S);
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      v4f sum = v4f{0, 0, 0, 0};
-      for (int b = 0; b < S; ++b) {
-        const float* src = frag(b, t, mb);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sum[j] += __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      const int v = (t * MB + mb) * 4;
+      const v4f sum = v4f{tot[v], tot[v + 1], tot[v + 2], tot[v + 3]};
       const int m = m0 + 16 * mb + (l & 15), n = (tile0 + t) * 16 + 4 * g;
       if (m < p.M && tile0 + t < ntiles) store_bf16x4(m, n, MX ? sum * p.as[m] : sum);
     }
@@ -339,22 +340,34 @@ constexpr size_t kMaxDecodeLds = 160 * 1024 - 256;
 
 // Tile-waves (TW), K-waves (KW), n-tiles per wave (T) and K steps per wave
 // (R) for a small-M shape; S workgroups split the rest of K.  Chosen from
-// sweeps of the decode shapes on MI355X: for M <= 16 the activation slice is
-// small, so one or two tiles per workgroup and many K-waves keep thousands of
-// waves streaming; for larger M the slice (8 KiB per step at M = 64) is shared
-// by 4-8 tiles over fewer steps.  MXFP4 needs R % 4 == 0 (one e8m0 dword per
-// lane covers four steps).
+// sweeps of the decode shapes on MI355X (graph-replayed, weights pooled past
+// the Infinity Cache): for M <= 16 the activation slice is small, so one or
+// two tiles per workgroup and many K-waves keep thousands of waves streaming;
+// for larger M the slice (8 KiB per step at M = 64) is shared by 4-8 tiles
+// over fewer steps.  Long K (>= 96 steps) and wide N (>= 512 tiles) run
+// 8-wave workgroups with a 64 KiB slice, two per CU, which split K further
+// now that the split-K reduction costs a few round trips (M = 32 / 64:
+// K = 17408 8-15% and N = 10240 10-14% faster than the 16-wave workgroup,
+// which stays best at N = K = 5120).  MXFP4 needs R % 4 == 0 (one e8m0 dword
+// per lane covers four steps).
 DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   DecodeCfg d{};
   d.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   d.mblocks = (M + 16 * d.mb - 1) / (16 * d.mb);
   d.rs = std::min(M, 16 * d.mb);
+  const bool long_k = KS >= 96, wide_n = N / 16 >= 512;
+  auto set = [&](int tw, int kw, int t, int r) { d.tw = tw; d.kw = kw; d.t = t; d.r = r; };
   if (d.mb == 1) {
-    if (mx) { d.tw = 1; d.kw = 10; d.t = 1; d.r = 4; }
-    else    { d.tw = 2; d.kw = 8; d.t = 1; d.r = 5; }
+    if (mx) long_k ? set(4, 2, 1, 8) : set(1, 10, 1, 4);
+    else    set(2, 8, 1, 5);
+  } else if (mx) {
+    set(8, 1, 1, 8);
+  } else if (long_k) {
+    d.mb == 2 ? set(4, 2, 1, 8) : set(4, 2, 1, 4);
+  } else if (wide_n) {
+    set(8, 1, 1, 8);
   } else {
-    if (mx) { d.tw = 8; d.kw = 1; d.t = 1; d.r = 8; }
-    else    { d.tw = 4; d.kw = 4; d.t = 1; d.r = 4; }
+    d.mb == 2 ? set(4, 2, 1, 4) : set(4, 4, 1, 4);
   }
   const int ntiles = N / 16;
   d.groups = (ntiles + d.tw * d.t - 1) / (d.tw * d.t);
@@ -418,14 +431,23 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     if (attr != hipSuccess) return BS_ERR_LAUNCH;                                                          \
     fn<<<grid, block, lds, st>>>(p);                                                                       \
   } while (0)
+  // one instantiation per configuration decode_cfg can return
+  const int key = d.tw * 10000 + d.kw * 100 + d.r;  // T == 1 everywhere; KW, R < 100
   if (mx) {
-    if (d.mb == 1) BS_DEC(true, 1, 1, 10, 1, 4);
-    else if (d.mb == 2) BS_DEC(true, 2, 8, 1, 1, 8);
-    else BS_DEC(true, 4, 8, 1, 1, 8);
+    if (d.mb == 1 && key == 11004) BS_DEC(true, 1, 1, 10, 1, 4);
+    else if (d.mb == 1 && key == 40208) BS_DEC(true, 1, 4, 2, 1, 8);
+    else if (d.mb == 2 && key == 80108) BS_DEC(true, 2, 8, 1, 1, 8);
+    else if (d.mb == 4 && key == 80108) BS_DEC(true, 4, 8, 1, 1, 8);
+    else return BS_ERR_SHAPE;
   } else {
-    if (d.mb == 1) BS_DEC(false, 1, 2, 8, 1, 5);
-    else if (d.mb == 2) BS_DEC(false, 2, 4, 4, 1, 4);
-    else BS_DEC(false, 4, 4, 4, 1, 4);
+    if (d.mb == 1 && key == 20805) BS_DEC(false, 1, 2, 8, 1, 5);
+    else if (d.mb == 2 && key == 40204) BS_DEC(false, 2, 4, 2, 1, 4);
+    else if (d.mb == 2 && key == 40208) BS_DEC(false, 2, 4, 2, 1, 8);
+    else if (d.mb == 2 && key == 80108) BS_DEC(false, 2, 8, 1, 1, 8);
+    else if (d.mb == 4 && key == 40404) BS_DEC(false, 4, 4, 4, 1, 4);
+    else if (d.mb == 4 && key == 40204) BS_DEC(false, 4, 4, 2, 1, 4);
+    else if (d.mb == 4 && key == 80108) BS_DEC(false, 4, 8, 1, 1, 8);
+    else return BS_ERR_SHAPE;
   }
 #undef BS_DEC
   return bs_launch_status();

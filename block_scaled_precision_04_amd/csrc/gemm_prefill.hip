@@ -377,18 +377,18 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     last = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!last) return;
+  {
+    // value (p, q, r) of split b sits at slot(b, p, q) + 64 r = slot(0, 0, 0) + b * split stride + 64 v
+    constexpr int kNV = C::kTN * C::kTM * 16;
+    float tot[kNV];
+    sum_partials<kNV, 64, 2>(tot, slot(0, 0, 0), static_cast<size_t>(gridDim.x) * (C::kWaves * kNV * 64), S);
 #pragma unroll
-  for (int p = 0; p < C::kTN; ++p)
+    for (int p = 0; p < C::kTN; ++p)
 #pragma unroll
-    for (int q = 0; q < C::kTM; ++q) {
-      acc[p][q] = v16f{};
-      for (int b = 0; b < S; ++b) {
-        const float* src = slot(b, p, q);
+      for (int q = 0; q < C::kTM; ++q)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[p][q][r] += __hip_atomic_load(src + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+        for (int r = 0; r < 16; ++r) acc[p][q][r] = tot[(p * C::kTM + q) * 16 + r];
+  }
   store_tile();
   if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -91,14 +91,16 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     last = __hip_atomic_fetch_add(&counters[nt], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ksplit - 1;
   __syncthreads();
   if (!last) return;
-  for (int o = threadIdx.x; o < MB * 256; o += 256) {
+  // output o = threadIdx.x + 256 i of split b sits at slab[(b * ntiles + nt) * MB * 256 + o]
+  float tot[MB];
+  sum_partials<MB, 256, 8>(tot, slab + static_cast<size_t>(nt) * (MB * 256) + threadIdx.x,
+                           static_cast<size_t>(ntiles) * (MB * 256), ksplit);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int o = threadIdx.x + 256 * i;
     const int lane = o & 63, rr = (o >> 6) & 3, mb = o >> 8;
-    float s = 0.0f;
-    for (int b = 0; b < ksplit; ++b)
-      s += __hip_atomic_load(&slab[(static_cast<size_t>(b) * ntiles + nt) * (MB * 256) + o], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
     const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
-    if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
+    if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(tot[i]));
   }
   if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -46,7 +46,10 @@ def test_fp8_block_small_workload():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 384), (65, 384, 640), (100, 128, 1024),
-                                   (64, 1280, 2048), (3, 5120, 17408)])
+                                   (64, 1280, 2048), (3, 5120, 17408),
+                                   # the 8-wave decode configurations: wide N (>= 512 tiles) and
+                                   # long K (>= 96 steps) at 17..32 and 33..64 rows, ragged M
+                                   (17, 8192, 384), (50, 8192, 256), (20, 256, 12288), (47, 128, 12288)])
 def test_fp8_block_edges(M, N, K):
     aq, asc, wq, wsc = fp8_block_inputs(9, M + N, M, N, K, outliers=True)
     got = _fp8_run(aq, asc, wq, wsc)
@@ -70,7 +73,7 @@ def _w4_run(aq, asc, wp, e, out=None):
 
 @pytest.mark.parametrize("M,N,K", [(8, 17408, 5120), (1, 16, 128), (33, 48, 384), (64, 176, 640),
                                    (13, 2048, 17408), (65, 48, 384), (129, 176, 640), (200, 1024, 1024),
-                                   (256, 1280, 5120), (300, 48, 17408)])
+                                   (256, 1280, 5120), (300, 48, 17408), (5, 48, 12288)])
 def test_w4a8_full_oracle(M, N, K):
     aq, asc, wp, e = w4a8_inputs(8, M + N + K, M, N, K)
     got = host_bits16(_w4_run(aq, asc, wp, e))
