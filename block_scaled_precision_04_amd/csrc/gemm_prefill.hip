@@ -417,9 +417,10 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
 // n_main / 256 a multiple of 256 / gcd(m_tiles, 256) -- and the remaining
 // column strip (less than one round of big tiles) runs as 128x128 tiles,
 // two workgroups per CU.  Small-tile grids under 256 tiles split K so that
-// about 512 workgroups run, keeping at least 8 K steps (1024 K) per split
-// (measured: 80 and 160 tiles gain from 6 and 3 splits; 256 tiles, such as
-// the column strips, run faster unsplit).  Below 256 big tiles everything
+// about 256 workgroups run, keeping at least 8 K steps (1024 K) per split
+// (measured with the batched split-K reduction: 80 tiles run fastest with 3
+// splits, 160 tiles unsplit -- 512 workgroups were 10-20% slower; 256 tiles,
+// such as the column strips, run faster unsplit).  Below 256 big tiles everything
 // runs as small tiles (that way 320 tiles ran 20% faster than as big ones).
 struct PrefillPlan {
   int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
@@ -441,7 +442,7 @@ PrefillPlan prefill_plan(int M, int N, int K) {
   const int ns = N - p.n_main;
   if (ns > 0) {
     p.tiles = ((M + 127) / 128) * ((ns + 127) / 128);
-    if (p.tiles < 256) p.s = std::max(1, std::min(512 / p.tiles, KS / 8));
+    if (p.tiles < 256) p.s = std::max(1, std::min(256 / p.tiles, KS / 8));
     p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
   }
   return p;
