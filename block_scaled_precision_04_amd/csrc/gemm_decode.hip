@@ -348,8 +348,10 @@ constexpr size_t kMaxDecodeLds = 160 * 1024 - 256;
 // 8-wave workgroups with a 64 KiB slice, two per CU, which split K further
 // now that the split-K reduction costs a few round trips (M = 32 / 64:
 // K = 17408 8-15% and N = 10240 10-14% faster than the 16-wave workgroup,
-// which stays best at N = K = 5120).  MXFP4 needs R % 4 == 0 (one e8m0 dword
-// per lane covers four steps).
+// which stays best at N = K = 5120).  At M <= 16, block-FP8 with at most 20
+// K steps runs 8-wave workgroups (M = 16 N = 512 K = 1024: 5.3 -> 4.2 us)
+// and wide N one tile per workgroup (M = 8 N = 10240: 13.1 -> 11.9 us).
+// MXFP4 needs R % 4 == 0 (one e8m0 dword per lane covers four steps).
 DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   DecodeCfg d{};
   d.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -358,8 +360,10 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   const bool long_k = KS >= 96, wide_n = N / 16 >= 512;
   auto set = [&](int tw, int kw, int t, int r) { d.tw = tw; d.kw = kw; d.t = t; d.r = r; };
   if (d.mb == 1) {
-    if (mx) long_k ? set(4, 2, 1, 8) : set(1, 10, 1, 4);
-    else    set(2, 8, 1, 5);
+    if (mx)               long_k ? set(4, 2, 1, 8) : set(1, 10, 1, 4);
+    else if (KS <= 20)    set(2, 4, 1, 5);    // few K steps: fewer idle K-waves
+    else if (wide_n && !long_k) set(1, 10, 1, 4);
+    else                  set(2, 8, 1, 5);
   } else if (mx) {
     set(8, 1, 1, 8);
   } else if (long_k) {
@@ -441,6 +445,8 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     else return BS_ERR_SHAPE;
   } else {
     if (d.mb == 1 && key == 20805) BS_DEC(false, 1, 2, 8, 1, 5);
+    else if (d.mb == 1 && key == 20405) BS_DEC(false, 1, 2, 4, 1, 5);
+    else if (d.mb == 1 && key == 11004) BS_DEC(false, 1, 1, 10, 1, 4);
     else if (d.mb == 2 && key == 40204) BS_DEC(false, 2, 4, 2, 1, 4);
     else if (d.mb == 2 && key == 40208) BS_DEC(false, 2, 4, 2, 1, 8);
     else if (d.mb == 2 && key == 80108) BS_DEC(false, 2, 8, 1, 1, 8);

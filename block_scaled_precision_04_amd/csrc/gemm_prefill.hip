@@ -378,10 +378,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   __syncthreads();
   if (!last) return;
   {
-    // value (p, q, r) of split b sits at slot(b, p, q) + 64 r = slot(0, 0, 0) + b * split stride + 64 v
+    // value (p, q, r) of split b sits at slot(b, p, q) + 64 r = slot(0, 0, 0) + b * split stride + 64 v;
+    // a split's 64 values per lane are one batch (two would not fit beside the tile in 256 registers)
     constexpr int kNV = C::kTN * C::kTM * 16;
     float tot[kNV];
-    sum_partials<kNV, 64, 2>(tot, slot(0, 0, 0), static_cast<size_t>(gridDim.x) * (C::kWaves * kNV * 64), S);
+    sum_partials<kNV, 64, 1>(tot, slot(0, 0, 0), static_cast<size_t>(gridDim.x) * (C::kWaves * kNV * 64), S);
 #pragma unroll
     for (int p = 0; p < C::kTN; ++p)
 #pragma unroll
