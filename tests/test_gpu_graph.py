@@ -1,0 +1,137 @@
+"""Every entry point under HIP graph capture: captured once, replayed several
+times with the program's own eager work and synchronizations between the
+replays, each replay bit-identical to the eager result.
+
+The library's contract for capture is that a call allocates, frees and
+synchronizes nothing, records no memset, and leaves its split-K workspace
+counters at zero (the last workgroup of a tile resets its counter), so the
+same workspace serves every replay.  The shapes cover the split-K paths of
+each GEMM (decode block-FP8 and W4A8 over several workgroups, the 8-wave
+long-K configurations, the small-tile W4A8 prefill split, the skinny GEMM's
+split), the block-FP8 tiled kernel, the W4A8 large-tile launch with its
+column strip (two dispatches in one call), and the producers and quantizers.
+The eager results themselves are checked against the oracle by the parity
+tests; here the graph must reproduce them exactly."""
+import pytest
+import torch
+
+import block_scaled_precision_04_amd as bs
+from block_scaled_precision_04_amd import synth
+from tests.gpu_util import dev_u8, dev_f32, dev_bf16, fp8_block_inputs, w4a8_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_call(M, N, K, seed):
+    aq, asc, wq, wsc = fp8_block_inputs(11, seed, M, N, K, outliers=True)
+    pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+    a, s, ws_ = dev_u8(aq), dev_f32(asc), dev_f32(wsc)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    work = bs.alloc_workspace(bs.BS_OP_FP8_BLOCK, M, N, K)
+    return (lambda: bs.bsgemm_fp8_block(a, s, desc, pre, ws_, out=out, ws=work)), [out]
+
+
+def _w4_call(M, N, K, seed):
+    aq, asc, wp, e = w4a8_inputs(12, seed, M, N, K)
+    pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
+    a, s = dev_u8(aq), dev_f32(asc)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    work = bs.alloc_workspace(bs.BS_OP_W4A8_MXFP4, M, N, K)
+    return (lambda: bs.bsgemm_w4a8_mxfp4(a, s, desc, pre, out=out, ws=work)), [out]
+
+
+def _skinny_call(M, N, K, seed):
+    xb, wb = synth.skinny_raw(seed, M, N, K)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    work = bs.alloc_workspace(bs.BS_OP_BF16_SKINNY, M, N, K)
+    return (lambda: bs.gemm_bf16_skinny(x, w, out=out, ws=work)), [out]
+
+
+def _producer_calls():
+    calls = []
+    M, K = 8, 5120
+    y, r, g = (dev_bf16(v) for v in synth.producer_raw(0, M, K))
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M,), dtype=torch.float32, device="cuda")
+    ro = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    calls.append(((lambda: bs.add_rms_quant_fp8(y, r, g, 1e-6, q, s, ro)), [q, s, ro]))
+    M2 = 64
+    y2, r2, g2 = (dev_bf16(v) for v in synth.producer_raw(1, M2, K))
+    q2 = torch.empty((M2, K), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((M2, K // 128), dtype=torch.float32, device="cuda")
+    ro2 = torch.empty((M2, K), dtype=torch.bfloat16, device="cuda")
+    calls.append(((lambda: bs.add_rms_quant_fp8_group128(y2, r2, g2, 1e-6, q2, s2, ro2)), [q2, s2, ro2]))
+    gu = dev_bf16(synth.silu_raw(0, 8, 17408))
+    q3 = torch.empty((8, 17408), dtype=torch.uint8, device="cuda")
+    s3 = torch.empty((8,), dtype=torch.float32, device="cuda")
+    calls.append(((lambda: bs.silu_mul_quant_fp8(gu, q3, s3)), [q3, s3]))
+    x = dev_bf16(synth.activation_raw(3, 0, 16, 1024))
+    q4 = torch.empty((16, 1024), dtype=torch.uint8, device="cuda")
+    s4 = torch.empty((16,), dtype=torch.float32, device="cuda")
+    q5 = torch.empty((16, 1024), dtype=torch.uint8, device="cuda")
+    s5 = torch.empty((16, 8), dtype=torch.float32, device="cuda")
+    calls.append(((lambda: bs.quant_fp8_per_token(x, q4, s4)), [q4, s4]))
+    calls.append(((lambda: bs.quant_fp8_group128(x, q5, s5)), [q5, s5]))
+    wb = dev_bf16(synth.fp8_block_raw(0, 0, 1, 256, 1024)[1])
+    q6 = torch.empty((256, 1024), dtype=torch.uint8, device="cuda")
+    s6 = torch.empty((2, 8), dtype=torch.float32, device="cuda")
+    calls.append(((lambda: bs.quant_fp8_block128(wb, q6, s6)), [q6, s6]))
+    return calls
+
+
+def _bits(t):
+    return t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+def test_graph_replays_match_eager():
+    calls = [
+        _fp8_call(8, 1280, 17408, 0),     # decode, K split over 4 workgroups
+        _fp8_call(64, 1280, 12288, 1),    # 8-wave long-K configuration, split
+        _fp8_call(40, 8192, 256, 2),      # wide N, 33..64 rows
+        _fp8_call(600, 384, 640, 3),      # tiled kernel (M >= 512)
+        _w4_call(8, 2048, 17408, 4),      # decode long-K configuration, split
+        _w4_call(256, 1280, 5120, 5),     # small-tile prefill, K split
+        _w4_call(4096, 5120, 1024, 6),    # large tiles + column strip
+        _skinny_call(8, 256, 2048, 0),    # split over 4 workgroups
+        _skinny_call(64, 96, 5120, 9),    # split over 10 workgroups
+    ] + _producer_calls()
+    # eager reference (twice: the second call checks the workspaces were left ready)
+    for fn, _ in calls:
+        fn()
+    torch.cuda.synchronize()
+    for fn, _ in calls:
+        fn()
+    torch.cuda.synchronize()
+    refs = [[_bits(o).clone() for o in outs] for _, outs in calls]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for fn, _ in calls:
+                fn()
+    torch.cuda.synchronize()
+
+    # unrelated eager work between replays, on its own buffers and workspace
+    other, other_outs = _fp8_call(32, 5120, 5120, 7)
+    for rep in range(4):
+        for _, outs in calls:
+            for o in outs:
+                o.zero_()
+        other()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for ci, (_, outs) in enumerate(calls):
+            for oi, o in enumerate(outs):
+                assert torch.equal(_bits(o), refs[ci][oi]), f"replay {rep}: call {ci} output {oi} differs from eager"
+        # and an eager call of the captured work still agrees afterwards
+        if rep == 1:
+            for fn, _ in calls:
+                fn()
+            torch.cuda.synchronize()
+            for ci, (_, outs) in enumerate(calls):
+                for oi, o in enumerate(outs):
+                    assert torch.equal(_bits(o), refs[ci][oi]), f"eager after replay: call {ci} output {oi}"
