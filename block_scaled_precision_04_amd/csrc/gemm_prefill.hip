@@ -421,7 +421,9 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
 // about 256 workgroups run, keeping at least 8 K steps (1024 K) per split
 // (measured with the batched split-K reduction: 80 tiles run fastest with 3
 // splits, 160 tiles unsplit -- 512 workgroups were 10-20% slower; 256 tiles,
-// such as the column strips, run faster unsplit).  Below 256 big tiles everything
+// such as the column strips, run faster unsplit, except over a long K: at
+// K = 17408 a 256-tile strip split in two took the M = 4096 N = 5120 launch
+// from 284 to 269 us).  Below 256 big tiles everything
 // runs as small tiles (that way 320 tiles ran 20% faster than as big ones).
 struct PrefillPlan {
   int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
@@ -444,6 +446,7 @@ PrefillPlan prefill_plan(int M, int N, int K) {
   if (ns > 0) {
     p.tiles = ((M + 127) / 128) * ((ns + 127) / 128);
     if (p.tiles < 256) p.s = std::max(1, std::min(256 / p.tiles, KS / 8));
+    if (p.tiles <= 256 && KS >= 96) p.s = std::max(p.s, 2);  // one round of tiles over a long K
     p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
   }
   return p;

@@ -91,6 +91,19 @@ def test_w4a8_prefill_workload_sampled(case):
     checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 prefill M={M} N={N} K={K}")
 
 
+def test_w4a8_down_projection_sampled():
+    """M=4096 N=5120 K=17408 (the SiLU chain's down projection): large tiles
+    over 4096 columns plus a 256-tile column strip whose K is split in two."""
+    M, N, K = 4096, 5120, 17408
+    aq, asc, wp, e = w4a8_inputs(5, 1, M, N, K)
+    got = host_bits16(_w4_run(aq, asc, wp, e))
+    rows, cols = sample_grid(M, N, 12, 40, seed=17)
+    cols = np.concatenate([cols, [4095, 4096, 4097, 5119]])
+    rows = np.concatenate([rows, [0, 1, M - 2, M - 1]])
+    _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 down projection M={M} N={N} K={K}")
+
+
 def test_w4a8_fused_chain():
     """The fused chain end to end: GPU producer -> GPU W4A8 GEMM against the
     oracle producer -> oracle GEMM on the same raw draws (the oracle never
