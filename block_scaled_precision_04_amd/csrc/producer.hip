@@ -6,7 +6,8 @@
 // _traced_quant: scale = max(rowamax/448, 1/(448*512)), fp32 math, clamp,
 // round-to-nearest cast).
 //
-// One 256-thread workgroup per row.  Each thread owns NC chunks of 8 bf16
+// One workgroup of T threads per row (256, or 128 for many short rows).
+// Each thread owns NC chunks of 8 bf16
 // (16-byte loads), keeps them in registers between the two row reductions
 // (sum of squares, then absolute maximum) and writes the e4m3 codes, so every
 // byte is read once and written once: 7 bytes per element plus 2 per column
@@ -27,22 +28,34 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Workgroup reductions over W waves (wave partials through LDS, added in wave order).
+template <int W = kThreads / 64>
 BS_INLINE float block_max(float v, float* red) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (l == 0) red[w] = v;
   __syncthreads();
-  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
 
+template <int W = kThreads / 64>
 BS_INLINE double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (l == 0) red[w] = v;
   __syncthreads();
-  double r = (red[0] + red[1]) + (red[2] + red[3]);
+  double r;
+  if constexpr (W == 4) {
+    r = (red[0] + red[1]) + (red[2] + red[3]);
+  } else {
+    r = red[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) r += red[i];
+  }
   __syncthreads();
   return r;
 }
@@ -75,14 +88,16 @@ BS_INLINE void unpack8(uint4 v, float* f) {
 // GROUP = true: one scale per 128-wide group of the row instead of one per
 // row; chunk idx = c*256 + t belongs to group idx/16, so the 16 consecutive
 // threads holding a group reduce its maximum with four shuffles.
-template <int NC, bool NORM, bool GROUP = false>
-__global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict__ y,
-                                                        const uint4* __restrict__ res,
-                                                        const uint4* __restrict__ gamma, float eps,
-                                                        uint2* __restrict__ q, float* __restrict__ scale,
-                                                        uint4* __restrict__ rout, int K) {
-  __shared__ double red_d[4];
-  __shared__ float red_f[4];
+template <int NC, bool NORM, bool GROUP = false, int T = kThreads>
+__global__ __launch_bounds__(T) void k_row_quant(const uint4* __restrict__ y,
+                                                 const uint4* __restrict__ res,
+                                                 const uint4* __restrict__ gamma, float eps,
+                                                 uint2* __restrict__ q, float* __restrict__ scale,
+                                                 uint4* __restrict__ rout, int K) {
+  static_assert(T % 64 == 0, "whole waves");
+  constexpr int kThreads = T;  // threads per row (shadows the file-wide default)
+  __shared__ double red_d[T / 64];
+  __shared__ float red_f[T / 64];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int nch = K >> 3;
@@ -128,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict_
     }
   }
   if constexpr (NORM) {
-    const double tot = block_sum_f64(ss, red_d);
+    const double tot = block_sum_f64<T / 64>(ss, red_d);
     const double inv = 1.0 / sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_row_quant(const uint4* __restrict_
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[c][j]));
-    amax = block_max(amax, red_f);
+    amax = block_max<T / 64>(amax, red_f);
     const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
     if (t == 0) scale[row] = s;
 #pragma unroll
@@ -317,9 +332,27 @@ int launch_silu_quant(const void* gu, void* q, float* scale, int M, int N, hipSt
   return bs_launch_status();
 }
 
+// Threads per row: 256 in general; with many rows (M >= 2048) and K <= 5120,
+// 128-thread rows of up to five chunks per thread, which keep more rows in
+// flight per CU (M = 8192, K = 5120: 63 -> 56 us, graph-replayed over inputs
+// pooled past the Infinity Cache).
 template <bool NORM, bool GROUP = false>
 int launch_row_quant(const void* y, const void* res, const void* gamma, float eps, void* q, float* scale,
                      void* rout, int M, int K, hipStream_t st) {
+  if (M >= 2048 && K <= 5120) {
+    const int nc = (K / 8 + 127) / 128;
+#define BS_ROWQ128(N_)                                                                                  \
+  k_row_quant<N_, NORM, GROUP, 128><<<dim3(M), dim3(128), 0, st>>>(                                    \
+      static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
+      static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
+    if (nc <= 1) BS_ROWQ128(1);
+    else if (nc <= 2) BS_ROWQ128(2);
+    else if (nc <= 3) BS_ROWQ128(3);
+    else if (nc <= 4) BS_ROWQ128(4);
+    else BS_ROWQ128(5);
+#undef BS_ROWQ128
+    return bs_launch_status();
+  }
   const int nc = (K / 8 + kThreads - 1) / kThreads;
   dim3 grid(M), block(kThreads);
 #define BS_ROWQ(N_)                                                                                    \

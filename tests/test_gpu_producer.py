@@ -30,7 +30,9 @@ def test_producer_fused_chain_sizes(case, M):
     print(rep)
 
 
-@pytest.mark.parametrize("M,K", [(1, 8), (3, 2056), (5, 1000), (2, 32768), (7, 640)])
+@pytest.mark.parametrize("M,K", [(1, 8), (3, 2056), (5, 1000), (2, 32768), (7, 640),
+                                 # many rows: the 128-thread row workgroups (1..5 chunks per thread)
+                                 (2048, 1032), (2050, 8), (2304, 5120)])
 def test_producer_ragged_shapes(M, K):
     g = synth.rng(700 + K)
     y = synth.bf16_normal(g, (M, K), 1.0)
@@ -58,12 +60,13 @@ def test_producer_special_rows_and_inplace():
     assert qg[2, 17] == 0xFE
 
 
-def test_quant_per_token():
-    g = synth.rng(11)
-    x = synth.bf16_normal(g, (64, 5120), 1.0)
+@pytest.mark.parametrize("M,K", [(64, 5120), (2048, 3080)])
+def test_quant_per_token(M, K):
+    g = synth.rng(11 + K)
+    x = synth.bf16_normal(g, (M, K), 1.0)
     q, s = bs.quant_fp8_per_token(dev_bf16(x))
     qo, so = quant.quant_per_token_bf16(x)
-    checks.assert_codes_close(host_u8(q), s.cpu().numpy(), qo, so, "per-token")
+    checks.assert_codes_close(host_u8(q), s.cpu().numpy(), qo, so, f"per-token M={M} K={K}")
 
 
 def test_quant_group_and_block():
@@ -127,7 +130,7 @@ def test_silu_mul_quant_special_rows(M):
 
 
 # ----------------------------------------------------------------- group-scale norm producer
-@pytest.mark.parametrize("M,K", [(1, 128), (3, 2048), (5, 5120), (2, 32768), (300, 640)])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 2048), (5, 5120), (2, 32768), (300, 640), (2048, 1152)])
 def test_group_producer_shapes(M, K):
     g = synth.rng(800 + K)
     y = synth.bf16_normal(g, (M, K), 1.0)
