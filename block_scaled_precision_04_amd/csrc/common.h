@@ -125,6 +125,15 @@ BS_INLINE void xcd_tile(int b, int m_tiles, int n_tiles, int group_m, int& mt, i
   nt = loc / gsize;
 }
 
+// Split-K workspaces (every GEMM that splits K across workgroups): the first
+// kWsCounterBytes hold the int32 tile counters, the fp32 slab of partials
+// starts right after them.  Counters are zero between launches (the last
+// workgroup of a tile resets its own), and no launch writes partials into the
+// counter region, so any sequence of calls -- of any shapes -- can share one
+// workspace that is large enough for each of them.
+constexpr size_t kWsCounterBytes = 64 * 1024;
+constexpr int kWsMaxCounters = static_cast<int>(kWsCounterBytes / sizeof(int));
+
 // Split-K reduction of the last-arriving workgroup: sum[v] = the S fp32
 // partials base[b * stride + v * VSTRIDE] added in split order b = 0, 1, ...
 // (deterministic).  The partials were written with device-scope stores, so

@@ -397,18 +397,31 @@ namespace {
 size_t slab_bytes(const DecodeCfg& d) {
   return static_cast<size_t>(d.s) * d.mblocks * d.groups * d.tw * d.t * d.mb * 256 * sizeof(float);
 }
-}  // namespace
 
-size_t bs_decode_workspace(int M, int N, int K, bool mx) {
-  // the largest of the row chunks' needs: full 64-row chunks and the remainder
-  size_t need = 0;
+// Workspace: kWsCounterBytes of counters (one per tile group and row block
+// of a launch), then the slab, sized for the largest of the call's row
+// chunks (full 64-row chunks and the remainder can differ in configuration).
+struct DecodeWs {
+  size_t slab;      // bytes
+  int max_counters;
+};
+DecodeWs decode_ws(int M, int N, int K, bool mx) {
+  DecodeWs w{0, 0};
   for (int rows : {std::min(M, kDecodeRows), M > kDecodeRows ? M % kDecodeRows : 0}) {
     if (rows <= 0) continue;
     const DecodeCfg d = decode_cfg(rows, N, K / 128, mx);
     if (d.s <= 1) continue;
-    need = std::max(need, (slab_bytes(d) + 255) / 256 * 256 + static_cast<size_t>(d.groups) * d.mblocks * sizeof(int));
+    w.slab = std::max(w.slab, slab_bytes(d));
+    w.max_counters = std::max(w.max_counters, d.groups * d.mblocks);
   }
-  return need;
+  return w;
+}
+
+}  // namespace
+
+size_t bs_decode_workspace(int M, int N, int K, bool mx) {
+  const DecodeWs w = decode_ws(M, N, K, mx);
+  return w.slab ? kWsCounterBytes + w.slab : 0;
 }
 
 namespace {
@@ -416,9 +429,8 @@ namespace {
 int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
   const DecodeCfg d = decode_cfg(p.M, p.N, p.KS, mx);
   if (d.s > 1) {
-    p.slab = static_cast<float*>(ws);
-    const size_t off = (slab_bytes(d) + 255) / 256 * 256;
-    p.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
+    p.counters = static_cast<int*>(ws);
+    p.slab = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
   p.rs = d.rs;
   dim3 grid(d.groups, d.s, d.mblocks);
@@ -465,6 +477,7 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
 int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, int64_t asm_, int64_t asg,
                                const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
                                void* work, hipStream_t st) {
+  if (decode_ws(M, N, K, false).max_counters > kWsMaxCounters) return BS_ERR_SHAPE;
   for (int r0 = 0; r0 < M; r0 += kDecodeRows) {
     DecodeArgs p{a + r0 * lda, lda, as + r0 * asm_, asm_, asg, w, ws, nullptr, c + r0 * ldc, ldc,
                  std::min(kDecodeRows, M - r0), N, K / 128, 0, nullptr, nullptr};
@@ -476,6 +489,7 @@ int bs_launch_fp8_block_decode(const uint8_t* a, int64_t lda, const float* as, i
 
 int bs_launch_w4a8_decode(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                           uint16_t* c, int64_t ldc, int M, int N, int K, void* work, hipStream_t st) {
+  if (decode_ws(M, N, K, true).max_counters > kWsMaxCounters) return BS_ERR_SHAPE;
   DecodeArgs p{a, lda, as, 0, 0, w, nullptr, wsc, c, ldc, M, N, K / 128, 0, nullptr, nullptr};
   return launch_decode(true, p, work, st);
 }

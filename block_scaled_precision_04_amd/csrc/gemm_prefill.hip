@@ -401,9 +401,9 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
   float* slab = nullptr;
   int* counters = nullptr;
   if (S > 1) {
-    slab = static_cast<float*>(ws);
-    counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) +
-                                      static_cast<size_t>(S) * tiles * BM * BN * sizeof(float));
+    if (tiles > kWsMaxCounters) return BS_ERR_SHAPE;  // split only below 256 tiles (prefill_plan)
+    counters = static_cast<int*>(ws);
+    slab = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
   k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
       a, static_cast<int>(lda), as, w, wsc, c, ldc, M, N, KS, group_m, slab, counters);
@@ -457,7 +457,7 @@ PrefillPlan prefill_plan(int M, int N, int K) {
 size_t bs_prefill_workspace(int M, int N, int K) {
   const PrefillPlan pl = prefill_plan(M, N, K);
   if (pl.tiles == 0 || pl.s <= 1) return 0;
-  return static_cast<size_t>(pl.s) * pl.tiles * 128 * 128 * sizeof(float) + static_cast<size_t>(pl.tiles) * sizeof(int);
+  return kWsCounterBytes + static_cast<size_t>(pl.s) * pl.tiles * 128 * 128 * sizeof(float);
 }
 
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,

@@ -119,7 +119,7 @@ size_t skinny_slab_bytes(int M, int N, int ks) {
 size_t bs_skinny_workspace(int M, int N, int K) {
   const int ks = bs_skinny_ksplit(K);
   if (ks <= 1) return 0;
-  return (skinny_slab_bytes(M, N, ks) + 255) / 256 * 256 + static_cast<size_t>(N / 16) * sizeof(int);
+  return kWsCounterBytes + skinny_slab_bytes(M, N, ks);
 }
 
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
@@ -128,9 +128,9 @@ int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, i
   float* slab = nullptr;
   int* counters = nullptr;
   if (ks > 1) {
-    slab = static_cast<float*>(ws);
-    const size_t off = (skinny_slab_bytes(M, N, ks) + 255) / 256 * 256;
-    counters = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + off);
+    if (N / 16 > kWsMaxCounters) return BS_ERR_SHAPE;  // one counter per 16-column tile
+    counters = static_cast<int*>(ws);
+    slab = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
   dim3 grid(N / 16, ks);
   if (M <= 16) k_skinny<1><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);

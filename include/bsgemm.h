@@ -123,12 +123,17 @@ BS_API int bs_unprelayout_mxfp4(const bs_wdesc* desc, const void* pre, void* w_p
 
 /* ---------------------------------------------------------- workspaces
  * Some shapes split K across workgroups and reduce through a caller-provided
- * workspace (fp32 partial slab + int32 counters, as the pages' decode split-K
+ * workspace (int32 counters + fp32 partial slab, as the pages' decode split-K
  * scratch: allocated once outside graph capture, zeroed once; the last
  * workgroup to finish a tile reduces it in a fixed order and resets its
  * counter, so the workspace is left zeroed-ready for the next call).  The
- * caller zero-fills it ONCE after allocation.  Calls that share a workspace
- * must be ordered (same stream); 0 means no workspace is needed. */
+ * caller zero-fills it ONCE after allocation.  Layout: the first 64 KiB hold
+ * the counters, the partials follow; no call writes partials into the counter
+ * region, so one workspace may serve any sequence of calls, of any ops and
+ * shapes, whose bs_workspace_bytes it covers.  Calls that share a workspace
+ * must be ordered (same stream); 0 means no workspace is needed.  A split
+ * that would need more than 16384 counters (one per 16-column tile group)
+ * is refused with BS_ERR_SHAPE. */
 enum { BS_OP_FP8_BLOCK = 1, BS_OP_W4A8_MXFP4 = 2, BS_OP_BF16_SKINNY = 3 };
 BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
 

@@ -57,6 +57,51 @@ def test_fp8_block_edges(M, N, K):
     checks.assert_gemm_close(got, ce, asum, f"fp8 block edge M={M} N={N} K={K}")
 
 
+# M in 65..511 runs as 64-row launches that share the workspace; the remainder
+# chunk can take another configuration than the full chunks (these shapes
+# once put its split-K counters inside the full chunks' partials).
+@pytest.mark.parametrize("M,N,K", [(408, 8448, 1408), (469, 640, 17280), (138, 768, 16384), (269, 640, 12288),
+                                   (401, 1408, 2816)])
+def test_fp8_block_row_chunks_sampled(M, N, K):
+    aq, asc, wq, wsc = fp8_block_inputs(10, M + K, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc)
+    rows, cols = sample_grid(M, N, 24, 40, seed=M)
+    _, ce, asum = gemm.fp8_block_gemm_at(aq, asc, wq, wsc, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, f"fp8 block row chunks M={M} N={N} K={K}")
+
+
+def test_shared_workspace_across_shapes():
+    """One workspace, zeroed once, serves a sequence of calls of every GEMM at
+    different shapes (split and unsplit, chunked rows with differing
+    configurations); each output equals the same call on a fresh workspace."""
+    calls = []
+    for (M, N, K) in [(100, 1280, 12288), (8, 1280, 17408), (40, 8192, 256), (21, 640, 17280)]:
+        aq, asc, wq, wsc = fp8_block_inputs(13, M + N, M, N, K, outliers=True)
+        pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+        args = (dev_u8(aq), dev_f32(asc), desc, pre, dev_f32(wsc))
+        calls.append((bs.BS_OP_FP8_BLOCK, (M, N, K), lambda ws, a=args: bs.bsgemm_fp8_block(*a, ws=ws)))
+    for (M, N, K) in [(8, 2048, 17408), (256, 1280, 5120), (40, 512, 5120)]:
+        aq, asc, wp, e = w4a8_inputs(14, M + N, M, N, K)
+        pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
+        args = (dev_u8(aq), dev_f32(asc), desc, pre)
+        calls.append((bs.BS_OP_W4A8_MXFP4, (M, N, K), lambda ws, a=args: bs.bsgemm_w4a8_mxfp4(*a, ws=ws)))
+    for (M, N, K) in [(8, 256, 2048), (64, 96, 5120)]:
+        xb, wb = synth.skinny_raw(M, M, N, K)
+        args = (dev_bf16(xb), dev_bf16(wb))
+        calls.append((bs.BS_OP_BF16_SKINNY, (M, N, K), lambda ws, a=args: bs.gemm_bf16_skinny(*a, ws=ws)))
+    need = max(bs.workspace_bytes(op, *shape) for op, shape, _ in calls)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    refs = []
+    for op, shape, fn in calls:
+        fresh = bs.alloc_workspace(op, *shape)
+        refs.append(fn(fresh).view(torch.int16).clone())
+    for rep in range(2):
+        for (op, shape, fn), ref in zip(calls, refs):
+            got = fn(shared if bs.workspace_bytes(op, *shape) else None)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), ref), f"pass {rep}: op {op} shape {shape}"
+
+
 # ------------------------------------------------------------------ MXFP4 W4A8
 def _w4_run(aq, asc, wp, e, out=None):
     pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
