@@ -360,7 +360,12 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   const bool long_k = KS >= 96, wide_n = N / 16 >= 512;
   auto set = [&](int tw, int kw, int t, int r) { d.tw = tw; d.kw = kw; d.t = t; d.r = r; };
   if (d.mb == 1) {
-    if (mx)               long_k ? set(4, 2, 1, 8) : set(1, 10, 1, 4);
+    // MXFP4 at 16 staged rows: the 40-step slice (80 KiB) would leave one
+    // workgroup per CU, so halve the K-waves and give each wave two tiles
+    // (M = 16: N = 17408 20 -> 16 us, N = 34816 36 -> 26 us; M <= 15 keeps
+    // two workgroups per CU and the 10-wave configuration)
+    const bool slice_halves_lds = static_cast<size_t>(d.rs) * 40 * 128 > kMaxDecodeLds / 2;
+    if (mx)               long_k ? set(4, 2, 1, 8) : (slice_halves_lds ? set(1, 5, 2, 4) : set(1, 10, 1, 4));
     else if (KS <= 20)    set(2, 4, 1, 5);    // few K steps: fewer idle K-waves
     else if (wide_n && !long_k) set(1, 10, 1, 4);
     else                  set(2, 8, 1, 5);
@@ -448,23 +453,24 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     fn<<<grid, block, lds, st>>>(p);                                                                       \
   } while (0)
   // one instantiation per configuration decode_cfg can return
-  const int key = d.tw * 10000 + d.kw * 100 + d.r;  // T == 1 everywhere; KW, R < 100
+  const int key = ((d.tw * 100 + d.kw) * 10 + d.t) * 100 + d.r;  // TW, KW, R < 100, T < 10
   if (mx) {
-    if (d.mb == 1 && key == 11004) BS_DEC(true, 1, 1, 10, 1, 4);
-    else if (d.mb == 1 && key == 40208) BS_DEC(true, 1, 4, 2, 1, 8);
-    else if (d.mb == 2 && key == 80108) BS_DEC(true, 2, 8, 1, 1, 8);
-    else if (d.mb == 4 && key == 80108) BS_DEC(true, 4, 8, 1, 1, 8);
+    if (d.mb == 1 && key == 110104) BS_DEC(true, 1, 1, 10, 1, 4);
+    else if (d.mb == 1 && key == 402108) BS_DEC(true, 1, 4, 2, 1, 8);
+    else if (d.mb == 1 && key == 105204) BS_DEC(true, 1, 1, 5, 2, 4);
+    else if (d.mb == 2 && key == 801108) BS_DEC(true, 2, 8, 1, 1, 8);
+    else if (d.mb == 4 && key == 801108) BS_DEC(true, 4, 8, 1, 1, 8);
     else return BS_ERR_SHAPE;
   } else {
-    if (d.mb == 1 && key == 20805) BS_DEC(false, 1, 2, 8, 1, 5);
-    else if (d.mb == 1 && key == 20405) BS_DEC(false, 1, 2, 4, 1, 5);
-    else if (d.mb == 1 && key == 11004) BS_DEC(false, 1, 1, 10, 1, 4);
-    else if (d.mb == 2 && key == 40204) BS_DEC(false, 2, 4, 2, 1, 4);
-    else if (d.mb == 2 && key == 40208) BS_DEC(false, 2, 4, 2, 1, 8);
-    else if (d.mb == 2 && key == 80108) BS_DEC(false, 2, 8, 1, 1, 8);
-    else if (d.mb == 4 && key == 40404) BS_DEC(false, 4, 4, 4, 1, 4);
-    else if (d.mb == 4 && key == 40204) BS_DEC(false, 4, 4, 2, 1, 4);
-    else if (d.mb == 4 && key == 80108) BS_DEC(false, 4, 8, 1, 1, 8);
+    if (d.mb == 1 && key == 208105) BS_DEC(false, 1, 2, 8, 1, 5);
+    else if (d.mb == 1 && key == 204105) BS_DEC(false, 1, 2, 4, 1, 5);
+    else if (d.mb == 1 && key == 110104) BS_DEC(false, 1, 1, 10, 1, 4);
+    else if (d.mb == 2 && key == 402104) BS_DEC(false, 2, 4, 2, 1, 4);
+    else if (d.mb == 2 && key == 402108) BS_DEC(false, 2, 4, 2, 1, 8);
+    else if (d.mb == 2 && key == 801108) BS_DEC(false, 2, 8, 1, 1, 8);
+    else if (d.mb == 4 && key == 404104) BS_DEC(false, 4, 4, 4, 1, 4);
+    else if (d.mb == 4 && key == 402104) BS_DEC(false, 4, 4, 2, 1, 4);
+    else if (d.mb == 4 && key == 801108) BS_DEC(false, 4, 8, 1, 1, 8);
     else return BS_ERR_SHAPE;
   }
 #undef BS_DEC
