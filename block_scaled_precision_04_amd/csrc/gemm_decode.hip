@@ -359,16 +359,22 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   d.rs = std::min(M, 16 * d.mb);
   const bool long_k = KS >= 96, wide_n = N / 16 >= 512;
   auto set = [&](int tw, int kw, int t, int r) { d.tw = tw; d.kw = kw; d.t = t; d.r = r; };
-  if (d.mb == 1) {
-    // MXFP4 at 16 staged rows: the 40-step slice (80 KiB) would leave one
-    // workgroup per CU, so halve the K-waves and give each wave two tiles
-    // (M = 16: N = 17408 20 -> 16 us, N = 34816 36 -> 26 us; M <= 15 keeps
-    // two workgroups per CU and the 10-wave configuration)
+  if (d.mb == 1 && mx) {
+    // At 16 staged rows the 40-step slice (80 KiB) would leave one workgroup
+    // per CU, so halve the K-waves and give each wave two tiles (M = 16:
+    // N = 17408 20 -> 16 us, N = 34816 36 -> 26 us).  From 5 rows and 640
+    // tiles on, three tiles per workgroup share the slice (M = 8: N = 17408
+    // 12.7 -> 11.5 us, N = 34816 20.6 -> 17.7 us; slower at N = 5120 and
+    // below 5 rows).
     const bool slice_halves_lds = static_cast<size_t>(d.rs) * 40 * 128 > kMaxDecodeLds / 2;
-    if (mx)               long_k ? set(4, 2, 1, 8) : (slice_halves_lds ? set(1, 5, 2, 4) : set(1, 10, 1, 4));
-    else if (KS <= 20)    set(2, 4, 1, 5);    // few K steps: fewer idle K-waves
+    if (long_k) set(4, 2, 1, 8);
+    else if (slice_halves_lds) set(1, 5, 2, 4);
+    else if (M >= 5 && N / 16 >= 640) set(3, 5, 1, 8);
+    else set(1, 10, 1, 4);
+  } else if (d.mb == 1) {
+    if (KS <= 20) set(2, 4, 1, 5);  // few K steps: fewer idle K-waves
     else if (wide_n && !long_k) set(1, 10, 1, 4);
-    else                  set(2, 8, 1, 5);
+    else set(2, 8, 1, 5);
   } else if (mx) {
     set(8, 1, 1, 8);
   } else if (long_k) {
@@ -458,6 +464,7 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     if (d.mb == 1 && key == 110104) BS_DEC(true, 1, 1, 10, 1, 4);
     else if (d.mb == 1 && key == 402108) BS_DEC(true, 1, 4, 2, 1, 8);
     else if (d.mb == 1 && key == 105204) BS_DEC(true, 1, 1, 5, 2, 4);
+    else if (d.mb == 1 && key == 305108) BS_DEC(true, 1, 3, 5, 1, 8);
     else if (d.mb == 2 && key == 801108) BS_DEC(true, 2, 8, 1, 1, 8);
     else if (d.mb == 4 && key == 801108) BS_DEC(true, 4, 8, 1, 1, 8);
     else return BS_ERR_SHAPE;
