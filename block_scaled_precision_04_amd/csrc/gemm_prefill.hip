@@ -325,27 +325,49 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   }
   wait_vm<0>();
 
-  // ---- epilogue: x per-token scale, bf16 RNE, 8-byte stores
+  // ---- epilogue: x per-token scale, bf16 RNE, then through LDS so that each
+  // store instruction writes whole output rows.  A lane's MFMA results are
+  // four consecutive n of one m, and the 32 lanes of a half wave hold 32
+  // different rows: stored directly, every instruction would touch 32 rows.
+  // Instead each wave writes its 8-byte pieces into an LDS copy of the tile
+  // (row-major, BN * 2 bytes per row, 8-byte pieces XOR-swizzled by the low
+  // five row bits so the 32 rows of a write land in distinct banks), and
+  // then every wave stores whole rows: lane j of a row writes piece j.  The
+  // tile (at most 128 KiB) fits in the stage buffers, which are idle once
+  // every wave's loads have landed and its LDS reads are done.
   auto store_tile = [&]() {
+    constexpr int kPieces = BN / 4;                 // 8-byte pieces per row
+    constexpr int kRowsPerPass = C::kThreads / kPieces;
+    static_assert(BM * BN * 2 <= STAGES * C::kStage, "output tile must fit the stage buffers");
+    static_assert(C::kThreads % kPieces == 0 && BM % kRowsPerPass == 0, "store pass shape");
+    wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < C::kTM; ++q) {
-      const int m = m0 + arow[q];
-      if (m >= M) continue;
-      const float sc = as[m];
+      const int r = arow[q];
+      const float sc = as[min(m0 + r, M - 1)];
 #pragma unroll
       for (int p = 0; p < C::kTN; ++p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = n0 + wn * (BN / WN) + 32 * p + 8 * i + 4 * (l >> 5);
-          if (n < N) {
-            const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
-            const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
-            const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
-            const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
-            *reinterpret_cast<uint2*>(c + m * ldc + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-          }
+          const int piece = (wn * (BN / WN) + 32 * p + 8 * i) / 4 + (l >> 5);
+          const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
+          const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
+          const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
+          const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
+          *reinterpret_cast<uint2*>(lds + r * (BN * 2) + (piece ^ (r & 31)) * 8) =
+              make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         }
       }
+    }
+    __syncthreads();
+    const int j = tid % kPieces, r0 = tid / kPieces;
+    const bool n_ok = n0 + 4 * j < N;  // N % 16 == 0: a piece is wholly inside or outside
+#pragma unroll 4
+    for (int r = r0; r < BM; r += kRowsPerPass) {
+      const uint2 v = *reinterpret_cast<const uint2*>(lds + r * (BN * 2) + (j ^ (r & 31)) * 8);
+      if (n_ok && m0 + r < M) *reinterpret_cast<uint2*>(c + (m0 + r) * ldc + n0 + 4 * j) = v;
     }
   };
   if (!SPLIT || S == 1) {
