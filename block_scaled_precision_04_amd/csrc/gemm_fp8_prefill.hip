@@ -17,7 +17,8 @@
 // 128 (n).  The weight is the first MFMA operand (rows = n) and the
 // activation the second (rows = m), so lane l holds four consecutive n of the
 // single row m = l % 16 of each block: one activation scale per lane per
-// 16-row block and K step, and 8-byte output stores.  A wave's 128 columns
+// 16-row block and K step; the epilogue regroups the bf16 results in LDS so
+// that stores write whole output rows.  A wave's 128 columns
 // lie inside one 128-wide weight-scale block, so its weight scale is one
 // value per K step.
 //
@@ -198,20 +199,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
     __syncthreads();  // ... and every wave is done with buffer ks & 1
   }
 
-  // ---- epilogue: bf16 RNE, four consecutive n of one m per lane (8 bytes)
-  if (!live_n) return;
+  // ---- epilogue: bf16 RNE, then through LDS so that each store instruction
+  // writes whole output rows.  A lane holds four consecutive n of one m, and
+  // the 16 lanes of a quarter wave hold 16 different rows; each wave writes
+  // its 8-byte pieces into an LDS copy of the tile (row-major, 512 bytes per
+  // row, piece index XOR (row % 8) * 4, which puts the 64 pieces of one write
+  // on 32 distinct bank slots), then lane j of a row stores piece j with the
+  // non-temporal hint (the output is written once).  The
+  // tile (128 KiB) fits in the two stage buffers, idle after the last barrier
+  // of the loop.  Waves whose columns lie past N take part in the barrier;
+  // their pieces are never stored.
+  constexpr int kPieces = kBN / 4;
+  constexpr int kRowsPerPass = kThreads / kPieces;
+  static_assert(kBM * kBN * 2 <= 2 * kStage, "output tile must fit the stage buffers");
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
-    const int m = m0 + wm * (kBM / kWM) + mb * 16 + (l & 15);
-    if (m >= M) continue;
+    const int r = wm * (kBM / kWM) + mb * 16 + (l & 15);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const int n = ncol0 + nb * 16 + 4 * q;
+      const int piece = wn * (kBN / kWN / 4) + nb * 4 + q;
       const v4f v = acc[mb][nb];
       const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
       const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      *reinterpret_cast<uint2*>(c + static_cast<int64_t>(m) * ldc + n) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(lds + r * (kBN * 2) + (piece ^ ((r & 7) << 2)) * 8) = make_uint2(lo, hi);
     }
+  }
+  __syncthreads();
+  const int j = tid % kPieces, r0 = tid / kPieces;
+  const bool n_ok = n0 + 4 * j < N;
+#pragma unroll 4
+  for (int r = r0; r < kBM; r += kRowsPerPass) {
+    const uint2 v = *reinterpret_cast<const uint2*>(lds + r * (kBN * 2) + (j ^ ((r & 7) << 2)) * 8);
+    if (n_ok && m0 + r < M) st_stream8(reinterpret_cast<uint2*>(c + static_cast<int64_t>(m0 + r) * ldc + n0 + 4 * j), v.x, v.y);
   }
 }
 

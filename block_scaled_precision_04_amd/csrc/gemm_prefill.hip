@@ -23,8 +23,9 @@
 // index so that the fragment reads (32 rows, same chunk) spread over the LDS
 // banks.  The per-token activation scale multiplies the accumulator in the
 // epilogue, then bf16 RNE and store.  The first MFMA operand is the weight
-// (rows = n), the second the activation (rows = m), so each lane stores four
-// consecutive n of one m (8 bytes).  Which tile size runs where (and the
+// (rows = n), the second the activation (rows = m), so each lane holds four
+// consecutive n of one m; the epilogue regroups them in LDS into whole output
+// rows before storing.  Which tile size runs where (and the
 // column strip that avoids a partial last round of large tiles) is decided by
 // prefill_plan below.
 //
@@ -332,7 +333,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   // Instead each wave writes its 8-byte pieces into an LDS copy of the tile
   // (row-major, BN * 2 bytes per row, 8-byte pieces XOR-swizzled by the low
   // five row bits so the 32 rows of a write land in distinct banks), and
-  // then every wave stores whole rows: lane j of a row writes piece j.  The
+  // then every wave stores whole rows: lane j of a row writes piece j, with
+  // the non-temporal hint (the output is written once and never re-read
+  // here, so it should not displace operand lines from L2).  The
   // tile (at most 128 KiB) fits in the stage buffers, which are idle once
   // every wave's loads have landed and its LDS reads are done.
   auto store_tile = [&]() {
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll 4
     for (int r = r0; r < BM; r += kRowsPerPass) {
       const uint2 v = *reinterpret_cast<const uint2*>(lds + r * (BN * 2) + (j ^ (r & 31)) * 8);
-      if (n_ok && m0 + r < M) *reinterpret_cast<uint2*>(c + (m0 + r) * ldc + n0 + 4 * j) = v;
+      if (n_ok && m0 + r < M) st_stream8(reinterpret_cast<uint2*>(c + (m0 + r) * ldc + n0 + 4 * j), v.x, v.y);
     }
   };
   if (!SPLIT || S == 1) {
