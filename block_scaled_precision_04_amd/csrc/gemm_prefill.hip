@@ -442,23 +442,28 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
 // column range [0, n_main) whose tile count is a whole number of rounds --
 // n_main / 256 a multiple of 256 / gcd(m_tiles, 256) -- and the remaining
 // column strip (less than one round of big tiles) runs as 128x128 tiles,
-// two workgroups per CU.  Small-tile grids under 256 tiles split K so that
-// about 256 workgroups run, keeping at least 8 K steps (1024 K) per split
-// (measured with the batched split-K reduction: 80 tiles run fastest with 3
-// splits, 160 tiles unsplit -- 512 workgroups were 10-20% slower; 256 tiles,
-// such as the column strips, run faster unsplit, except over a long K: at
-// K = 17408 a 256-tile strip split in two took the M = 4096 N = 5120 launch
-// from 284 to 269 us).  Below 256 big tiles everything
-// runs as small tiles (that way 320 tiles ran 20% faster than as big ones).
+// two workgroups per CU.  Below 256 big tiles everything runs as small tiles
+// (that way 320 tiles ran 20% faster than as big ones).  The small tiles
+// have the same problem one level down: more than 512 of them (two per CU)
+// with a partial last round are cut the same way, the widest column range
+// [n_main, n_mid) that fills whole rounds runs unsplit, and only the
+// remaining columns go to the split launch.  Small-tile grids under 256
+// tiles split K so that about 256 workgroups run, keeping at least 8 K steps
+// (1024 K) per split (measured with the batched split-K reduction: 80 tiles
+// run fastest with 3 splits, 160 tiles unsplit -- 512 workgroups were 10-20%
+// slower; 256 tiles, such as the column strips, run faster unsplit, except
+// over a long K: at K = 17408 a 256-tile strip split in two took the
+// M = 4096 N = 5120 launch from 284 to 269 us).
 struct PrefillPlan {
   int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
-  int s;        // K splits of the small-tile launch over columns [n_main, N)
-  int tiles;    // small tiles (0: none)
+  int n_mid;    // columns [n_main, n_mid) as unsplit 128x128 tiles, whole rounds of 512
+  int s;        // K splits of the small-tile launch over columns [n_mid, N)
+  int tiles;    // small tiles of that launch (0: none)
 };
 PrefillPlan prefill_plan(int M, int N, int K) {
   const int KS = K / 128;
   const int mt = (M + 255) / 256, nt = (N + 255) / 256;
-  PrefillPlan p{0, 1, 0};
+  PrefillPlan p{0, 0, 1, 0};
   if (mt * nt >= 256) {
     p.n_main = N;
     if ((mt * nt) % 256 != 0) {
@@ -467,9 +472,17 @@ PrefillPlan prefill_plan(int M, int N, int K) {
       if (n1 >= 1 && mt * (nt - n1) < 256) p.n_main = n1 * 256;
     }
   }
-  const int ns = N - p.n_main;
+  p.n_mid = p.n_main;
+  const int mts = (M + 127) / 128;
+  const int nts = (N - p.n_main + 127) / 128;
+  if (mts * nts > 512 && (mts * nts) % 512 != 0) {
+    const int g = 512 / std::gcd(mts, 512);
+    const int n1 = (nts - 1) / g * g;
+    if (n1 >= 1) p.n_mid = p.n_main + n1 * 128;
+  }
+  const int ns = N - p.n_mid;
   if (ns > 0) {
-    p.tiles = ((M + 127) / 128) * ((ns + 127) / 128);
+    p.tiles = mts * ((ns + 127) / 128);
     if (p.tiles < 256) p.s = std::max(1, std::min(256 / p.tiles, KS / 8));
     if (p.tiles <= 256 && KS >= 96) p.s = std::max(p.s, 2);  // one round of tiles over a long K
     p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
@@ -495,11 +508,18 @@ int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const
                                                                nullptr, st);
     if (rc != BS_OK || pl.tiles == 0) return rc;
   }
-  // the column strip: the weight's n-tiles from n_main / 16 on (codes KS KiB
-  // and scales ceil(KS/4) * 256 bytes per 16-column tile), output columns
-  // from n_main on
-  const size_t nt_off = static_cast<size_t>(pl.n_main) / 16;
-  return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w + nt_off * KS * 1024,
-                                                    sc + nt_off * ((KS + 3) / 4) * 256, c + pl.n_main, ldc, M,
-                                                    N - pl.n_main, KS, 4, pl.s, ws, st);
+  // a small-tile launch over columns [n0, n1): the weight's n-tiles from
+  // n0 / 16 on (codes KS KiB and scales ceil(KS/4) * 256 bytes per
+  // 16-column tile), output columns from n0 on
+  auto small = [&](int n0, int n1, int s, void* work) {
+    const size_t nt_off = static_cast<size_t>(n0) / 16;
+    return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w + nt_off * KS * 1024,
+                                                      sc + nt_off * ((KS + 3) / 4) * 256, c + n0, ldc, M, n1 - n0,
+                                                      KS, 4, s, work, st);
+  };
+  if (pl.n_mid > pl.n_main) {
+    const int rc = small(pl.n_main, pl.n_mid, 1, nullptr);
+    if (rc != BS_OK || pl.tiles == 0) return rc;
+  }
+  return small(pl.n_mid, N, pl.s, ws);
 }

@@ -312,6 +312,27 @@ def test_w4a8_prefill_column_strip():
     checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 column strip")
 
 
+def test_w4a8_prefill_small_tile_rounds():
+    """Both levels of the tile plan.  M=2048, N=13392: 8 x 53 large tiles ->
+    the large-tile launch takes 8192 columns (256 tiles, one round), the
+    5200-column strip is 16 x 41 small tiles, of which 4096 columns (512
+    tiles, one round of two per CU) run unsplit and the last 1104 columns
+    (144 tiles) in a third launch.  M=500, N=17456, K=2048: 2 x 69 large
+    tiles (too few), 4 x 137 = 548 small tiles -> 16384 columns unsplit and
+    the last 1072 columns (36 tiles) split in K.  Samples cover every launch
+    and the seams between them."""
+    for seed, (M, N, K), seams in ((11, (500, 17456, 2048), [16383, 16384, 16399, 17455]),
+                                   (12, (2048, 13392, 1024), [8191, 8192, 12287, 12288, 13391])):
+        aq, asc, wp, e = w4a8_inputs(8, seed, M, N, K)
+        got = host_bits16(_w4_run(aq, asc, wp, e))
+        rows, cols = sample_grid(M, N, 12, 24, seed=seed)
+        rr, cc = np.meshgrid(np.unique(np.r_[rows, [0, M - 1]]), np.array(seams), indexing="ij")
+        rows = np.r_[rows, rr.reshape(-1)]
+        cols = np.r_[cols, cc.reshape(-1)]
+        _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+        checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 tile rounds M={M} N={N} K={K}")
+
+
 def test_empty_batch_through_the_binding():
     """Zero-row inputs (torch may hand out NULL data pointers for them) give
     empty outputs and no error, for every GEMM and producer."""
