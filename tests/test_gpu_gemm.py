@@ -191,6 +191,31 @@ def test_w4a8_no_out_of_bounds_writes_and_ldc():
     checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 strided out")
 
 
+def test_w4a8_large_tiles_strided_out():
+    """The large-tile launch and its column strip writing into a strided view:
+    M=4000 (last 256-row tile 160 rows deep), N=4240 -> 16 x 16 large tiles
+    over 4096 columns plus a 144-column strip of split small tiles.  Nothing
+    outside the view changes; sampled values (seams included) match the
+    oracle."""
+    M, N, K = 4000, 4240, 2048
+    aq, asc, wp, e = w4a8_inputs(8, 13, M, N, K)
+    big = torch.full((M + 2, N + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[1:M + 1, 8:8 + N]
+    _w4_run(aq, asc, wp, e, out=view)
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[1:M + 1, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    got = host_bits16(view.contiguous())
+    rows, cols = sample_grid(M, N, 12, 24, seed=13)
+    rr, cc = np.meshgrid(np.array([0, 255, 256, 3839, 3840, M - 1]), np.array([4095, 4096, 4223, 4224, N - 1]),
+                         indexing="ij")
+    rows = np.r_[rows, rr.reshape(-1)]
+    cols = np.r_[cols, cc.reshape(-1)]
+    _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 large tiles strided out")
+
+
 def test_determinism():
     M, N, K = 256, 1280, 5120
     aq, asc, wp, e = w4a8_inputs(8, 2, M, N, K)
