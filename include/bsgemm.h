@@ -171,7 +171,9 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
  * elements, multiple of 4).  Needs M >= 1, N % 16 == 0, K % 128 == 0.
  * Small M (<= 64) streams the weight (bandwidth-bound); large M runs the
  * LDS-tiled scaled-MFMA kernel (compute-bound; a grid whose large tiles end
- * in a partial round runs its last columns as small tiles).  Whenever either
+ * in a partial round runs its last columns as small tiles, and a small-tile
+ * grid that ends in a partial round runs its last columns as a separate
+ * split launch; every launch is on the given stream, in order).  Whenever either
  * splits K across workgroups (small grids, column strips) the call needs ws
  * of bs_workspace_bytes(BS_OP_W4A8_MXFP4, M, N, K) bytes (256-byte aligned,
  * zeroed once); when that is 0, ws may be NULL.
