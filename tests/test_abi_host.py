@@ -137,6 +137,24 @@ def test_prelayout_validation(blib):
     assert blib.bs_unprelayout_fp8_block(ctypes.byref(d), FAKE, FAKE, None) == -4             # empty descriptor
 
 
+@pytest.mark.parametrize("M,N,K,splits,tiles", [
+    (256, 5120, 17408, 3, 80),      # 80 small tiles (< 256): K split three ways
+    (256, 34816, 5120, 5, 32),      # 544 small tiles: 512 unsplit, the last 32 split five ways
+    (500, 17456, 2048, 2, 36),      # 548 small tiles: 512 unsplit, the last 36 split in two
+    (2048, 5120, 17408, 2, 128),    # 640 small tiles: 512 unsplit, the last 128 split in two (long K)
+    (4096, 5120, 17408, 2, 256),    # 256 large tiles + a 256-small-tile strip split in two (long K)
+    (2048, 17408, 5120, 2, 128),    # 1024 large tiles (4 rounds) + 128-tile strip split in two
+    (2048, 10240, 5120, 1, 256),    # 256 large tiles + a 256-small-tile strip, unsplit
+    (8192, 34816, 5120, 1, 0),      # 4352 large tiles (17 rounds), nothing else
+])
+def test_w4a8_prefill_plan_workspace(blib, M, N, K, splits, tiles):
+    """The large-M W4A8 tile plan, seen through the workspace query: a split
+    launch needs the 64 KiB counter region plus splits x tiles fp32 128x128
+    partial tiles; an unsplit plan needs none."""
+    want = 0 if splits <= 1 else 64 * 1024 + splits * tiles * 128 * 128 * 4
+    assert blib.bs_workspace_bytes(2, M, N, K) == want
+
+
 def test_offset_range_limits(blib):
     """Shapes whose 32-bit in-kernel offsets would overflow are refused on the
     host: block-FP8 tiled path lda < 2^24, W4A8 N*K/2 < 2^32."""
