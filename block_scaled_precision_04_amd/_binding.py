@@ -101,6 +101,49 @@ def _u8(t):
     return t.view(torch.uint8) if t.dtype != torch.uint8 else t
 
 
+# ---------------------------------------------------------------- argument checks
+# The library sees raw pointers and sizes only, so every tensor's shape, dtype
+# and row stride is checked here before the call: a wrong output tensor would
+# otherwise be written as if it were a dense [M, N] buffer.
+_FP8 = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _need(cond, fn, msg):
+    if not cond:
+        raise ValueError(f"{fn}: {msg}")
+
+
+def _arg(fn, name, t, shape, dtypes, contiguous=False, unit_inner=True):
+    """t must have `shape` and one of `dtypes`; its last dimension must be
+    unit-stride (rows may be padded) or, with contiguous=True, the tensor dense."""
+    _need(t is not None, fn, f"{name} is required")
+    _need(isinstance(t, torch.Tensor), fn, f"{name} must be a torch.Tensor")
+    _need(t.dtype in dtypes, fn, f"{name} has dtype {t.dtype}, expected one of {tuple(str(d) for d in dtypes)}")
+    _need(tuple(t.shape) == tuple(shape), fn, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contiguous:
+        _need(t.is_contiguous(), fn, f"{name} must be contiguous")
+    elif unit_inner and t.dim() >= 2 and t.shape[-1] > 1:
+        _need(t.stride(-1) == 1, fn, f"{name} must have unit stride along its last dimension")
+        _need(t.stride(0) >= t.shape[-1], fn, f"{name} rows overlap (stride {t.stride(0)} < {t.shape[-1]})")
+    return t
+
+
+def _on_device(fn, *ts):
+    """Every tensor lives on the same GPU (a host tensor would hand the kernels a host address)."""
+    devs = {t.device for t in ts if t is not None}
+    _need(all(d.type == "cuda" for d in devs), fn, f"tensors must be on a GPU, got {sorted(map(str, devs))}")
+    _need(len(devs) <= 1, fn, f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def _ws(fn, ws):
+    """(pointer, bytes) of an optional workspace tensor (dense, any dtype)."""
+    if ws is None:
+        return None, 0
+    _need(isinstance(ws, torch.Tensor) and ws.is_contiguous(), fn, "ws must be a contiguous tensor")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 def _bits16(t):
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return t
@@ -169,13 +212,24 @@ def bsgemm_fp8_block(a, a_scale, desc, w_pre, w_scale, out=None, ws=None):
     """C[M,N] bf16 = block-FP8 GEMM.  a: [M,K] e4m3 (row stride in bytes may be
     padded to a multiple of 16); a_scale: fp32 [M, K/128] with any strides;
     w_scale: fp32 [N/128, K/128] contiguous."""
-    a8 = _u8(a)
-    M, K = a8.shape
+    fn = "bsgemm_fp8_block"
+    _need(isinstance(a, torch.Tensor) and a.dim() == 2, fn, "a must be a 2-D tensor [M, K]")
+    M, K = a.shape
     N = desc.N
+    _need(desc.K == K, fn, f"a has K = {K}, the weight descriptor K = {desc.K}")
+    _arg(fn, "a", a, (M, K), _FP8)
+    _arg(fn, "a_scale", a_scale, (M, K // 128), (torch.float32,), unit_inner=False)
+    _arg(fn, "w_scale", w_scale, (N // 128, K // 128), (torch.float32,), unit_inner=False)
+    _arg(fn, "w_pre", w_pre, (w_pre.numel(),), (torch.uint8,), contiguous=True)
+    _need(w_pre.numel() >= desc.total_bytes, fn, f"w_pre holds {w_pre.numel()} bytes, the layout needs "
+                                                 f"{desc.total_bytes}")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a8.device)
-    ws_p, ws_n = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
-    _check("bsgemm_fp8_block", lib().bsgemm_fp8_block(
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _arg(fn, "out", out, (M, N), _BF16)
+    _on_device(fn, a, a_scale, w_pre, w_scale, out, ws)
+    a8 = _u8(a)
+    ws_p, ws_n = _ws(fn, ws)
+    _check(fn, lib().bsgemm_fp8_block(
         _ptr(a8), a8.stride(0), _ptr(a_scale), a_scale.stride(0), a_scale.stride(1), ctypes.byref(desc),
         _ptr(w_pre), _ptr(w_scale.contiguous()), _ptr(out), out.stride(0), M, N, K, ws_p, ws_n, _stream()))
     return out
@@ -183,13 +237,23 @@ def bsgemm_fp8_block(a, a_scale, desc, w_pre, w_scale, out=None, ws=None):
 
 def bsgemm_w4a8_mxfp4(a, a_scale, desc, w_pre, out=None, ws=None):
     """C[M,N] bf16 = MXFP4 W4A8 GEMM.  a: [M,K] e4m3; a_scale: fp32 [M]."""
-    a8 = _u8(a)
-    M, K = a8.shape
+    fn = "bsgemm_w4a8_mxfp4"
+    _need(isinstance(a, torch.Tensor) and a.dim() == 2, fn, "a must be a 2-D tensor [M, K]")
+    M, K = a.shape
     N = desc.N
+    _need(desc.K == K, fn, f"a has K = {K}, the weight descriptor K = {desc.K}")
+    _arg(fn, "a", a, (M, K), _FP8)
+    _arg(fn, "a_scale", a_scale, (M,), (torch.float32,), unit_inner=False)
+    _arg(fn, "w_pre", w_pre, (w_pre.numel(),), (torch.uint8,), contiguous=True)
+    _need(w_pre.numel() >= desc.total_bytes, fn, f"w_pre holds {w_pre.numel()} bytes, the layout needs "
+                                                 f"{desc.total_bytes}")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a8.device)
-    ws_p, ws_n = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
-    _check("bsgemm_w4a8_mxfp4", lib().bsgemm_w4a8_mxfp4(
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _arg(fn, "out", out, (M, N), _BF16)
+    _on_device(fn, a, a_scale, w_pre, out, ws)
+    a8 = _u8(a)
+    ws_p, ws_n = _ws(fn, ws)
+    _check(fn, lib().bsgemm_w4a8_mxfp4(
         _ptr(a8), a8.stride(0), _ptr(a_scale.contiguous()), ctypes.byref(desc), _ptr(w_pre), _ptr(out),
         out.stride(0), M, N, K, ws_p, ws_n, _stream()))
     return out
@@ -197,30 +261,62 @@ def bsgemm_w4a8_mxfp4(a, a_scale, desc, w_pre, out=None, ws=None):
 
 def gemm_bf16_skinny(x, w, out=None, ws=None):
     """C[M,N] bf16 = x[M,K] . w[N,K]^T (M <= 64).  ws: from alloc_workspace when K is split."""
-    x = _bits16(x).contiguous()
-    w = _bits16(w).contiguous()
+    fn = "gemm_bf16_skinny"
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2 and isinstance(w, torch.Tensor) and w.dim() == 2, fn,
+          "x [M, K] and w [N, K] must be 2-D tensors")
     M, K = x.shape
     N = w.shape[0]
+    _arg(fn, "x", x, (M, K), _BF16, unit_inner=False)
+    _arg(fn, "w", w, (N, K), _BF16, unit_inner=False)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    ws_p, ws_n = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
-    _check("gemm_bf16_skinny", lib().gemm_bf16_skinny(_ptr(x), _ptr(w), _ptr(out), M, N, K, ws_p, ws_n,
-                                                       _stream()))
+    _arg(fn, "out", out, (M, N), _BF16, contiguous=True)    # the C call takes no leading dimension for c
+    _on_device(fn, x, w, out, ws)
+    x = x.contiguous()
+    w = w.contiguous()
+    ws_p, ws_n = _ws(fn, ws)
+    _check(fn, lib().gemm_bf16_skinny(_ptr(x), _ptr(w), _ptr(out), M, N, K, ws_p, ws_n, _stream()))
     return out
 
 
 # ------------------------------------------------------------------ producers
-def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual_out=None):
-    """(q e4m3 [M,K] as uint8, scale fp32 [M], residual_out bf16 [M,K])."""
-    y = _bits16(y).contiguous()
-    residual = _bits16(residual).contiguous()
-    gamma = _bits16(gamma).contiguous()
+def _producer_args(fn, y, residual, gamma, q, scale, residual_out, group):
+    """Checked (y, residual, gamma, q, scale, residual_out) of the norm
+    producers; scale has one value per row (group = 1) or per 128 columns."""
+    _need(isinstance(y, torch.Tensor) and y.dim() == 2, fn, "y must be a 2-D tensor [M, K]")
     M, K = y.shape
     dev = y.device
+    _arg(fn, "y", y, (M, K), _BF16, unit_inner=False)
+    _arg(fn, "residual", residual, (M, K), _BF16, unit_inner=False)
+    _arg(fn, "gamma", gamma, (K,), _BF16, unit_inner=False)
+    sshape = (M,) if group == 1 else (M, K // 128)
     q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
-    scale = torch.empty((M,), dtype=torch.float32, device=dev) if scale is None else scale
+    scale = torch.empty(sshape, dtype=torch.float32, device=dev) if scale is None else scale
     residual_out = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if residual_out is None else residual_out
-    _check("add_rms_quant_fp8", lib().add_rms_quant_fp8(
+    _arg(fn, "q", q, (M, K), _FP8, contiguous=True)
+    _arg(fn, "scale", scale, sshape, (torch.float32,), contiguous=True)
+    _arg(fn, "residual_out", residual_out, (M, K), _BF16, contiguous=True)
+    _on_device(fn, y, residual, gamma, q, scale, residual_out)
+    return y.contiguous(), residual.contiguous(), gamma.contiguous(), q, scale, residual_out
+
+
+def _quant_args(fn, x, q, scale, qshape, sshape, in_shape=None):
+    """Checked (x, q, scale) of the quantizers."""
+    _arg(fn, "x", x, in_shape or qshape, _BF16, unit_inner=False)
+    q = torch.empty(qshape, dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(sshape, dtype=torch.float32, device=x.device) if scale is None else scale
+    _arg(fn, "q", q, qshape, _FP8, contiguous=True)
+    _arg(fn, "scale", scale, sshape, (torch.float32,), contiguous=True)
+    _on_device(fn, x, q, scale)
+    return x.contiguous(), q, scale
+
+
+def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual_out=None):
+    """(q e4m3 [M,K] as uint8, scale fp32 [M], residual_out bf16 [M,K])."""
+    fn = "add_rms_quant_fp8"
+    y, residual, gamma, q, scale, residual_out = _producer_args(fn, y, residual, gamma, q, scale, residual_out, 1)
+    M, K = y.shape
+    _check(fn, lib().add_rms_quant_fp8(
         _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
         M, K, _stream()))
     return q, scale, residual_out
@@ -228,15 +324,11 @@ def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual
 
 def add_rms_quant_fp8_group128(y, residual, gamma, eps=1e-6, q=None, scale=None, residual_out=None):
     """(q e4m3 [M,K] as uint8, scale fp32 [M, K/128], residual_out bf16 [M,K])."""
-    y = _bits16(y).contiguous()
-    residual = _bits16(residual).contiguous()
-    gamma = _bits16(gamma).contiguous()
+    fn = "add_rms_quant_fp8_group128"
+    y, residual, gamma, q, scale, residual_out = _producer_args(fn, y, residual, gamma, q, scale, residual_out,
+                                                                128)
     M, K = y.shape
-    dev = y.device
-    q = torch.empty((M, K), dtype=torch.uint8, device=dev) if q is None else q
-    scale = torch.empty((M, K // 128), dtype=torch.float32, device=dev) if scale is None else scale
-    residual_out = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if residual_out is None else residual_out
-    _check("add_rms_quant_fp8_group128", lib().add_rms_quant_fp8_group128(
+    _check(fn, lib().add_rms_quant_fp8_group128(
         _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
         M, K, _stream()))
     return q, scale, residual_out
@@ -244,37 +336,38 @@ def add_rms_quant_fp8_group128(y, residual, gamma, eps=1e-6, q=None, scale=None,
 
 def silu_mul_quant_fp8(gu, q=None, scale=None):
     """gu bf16 [M, 2N] (gate half first) -> (q e4m3 [M, N] as uint8, scale fp32 [M])."""
-    gu = _bits16(gu).contiguous()
+    fn = "silu_mul_quant_fp8"
+    _need(isinstance(gu, torch.Tensor) and gu.dim() == 2 and gu.shape[1] % 2 == 0, fn,
+          "gu must be a 2-D tensor [M, 2N]")
     M, N2 = gu.shape
     N = N2 // 2
-    q = torch.empty((M, N), dtype=torch.uint8, device=gu.device) if q is None else q
-    scale = torch.empty((M,), dtype=torch.float32, device=gu.device) if scale is None else scale
-    _check("silu_mul_quant_fp8", lib().silu_mul_quant_fp8(_ptr(gu), _ptr(q), _ptr(scale), M, N, _stream()))
+    gu, q, scale = _quant_args(fn, gu, q, scale, (M, N), (M,), in_shape=(M, N2))
+    _check(fn, lib().silu_mul_quant_fp8(_ptr(gu), _ptr(q), _ptr(scale), M, N, _stream()))
     return q, scale
 
 
 def quant_fp8_per_token(x, q=None, scale=None):
-    x = _bits16(x).contiguous()
+    fn = "quant_fp8_per_token"
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2, fn, "x must be a 2-D tensor [M, K]")
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    scale = torch.empty((M,), dtype=torch.float32, device=x.device) if scale is None else scale
-    _check("quant_fp8_per_token", lib().quant_fp8_per_token(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream()))
+    x, q, scale = _quant_args(fn, x, q, scale, (M, K), (M,))
+    _check(fn, lib().quant_fp8_per_token(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream()))
     return q, scale
 
 
 def quant_fp8_group128(x, q=None, scale=None):
-    x = _bits16(x).contiguous()
+    fn = "quant_fp8_group128"
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2, fn, "x must be a 2-D tensor [M, K]")
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    scale = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if scale is None else scale
-    _check("quant_fp8_group128", lib().quant_fp8_group128(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream()))
+    x, q, scale = _quant_args(fn, x, q, scale, (M, K), (M, K // 128))
+    _check(fn, lib().quant_fp8_group128(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream()))
     return q, scale
 
 
 def quant_fp8_block128(w, q=None, scale=None):
-    w = _bits16(w).contiguous()
+    fn = "quant_fp8_block128"
+    _need(isinstance(w, torch.Tensor) and w.dim() == 2, fn, "w must be a 2-D tensor [N, K]")
     N, K = w.shape
-    q = torch.empty((N, K), dtype=torch.uint8, device=w.device) if q is None else q
-    scale = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device) if scale is None else scale
-    _check("quant_fp8_block128", lib().quant_fp8_block128(_ptr(w), _ptr(q), _ptr(scale), N, K, _stream()))
+    w, q, scale = _quant_args(fn, w, q, scale, (N, K), (N // 128, K // 128))
+    _check(fn, lib().quant_fp8_block128(_ptr(w), _ptr(q), _ptr(scale), N, K, _stream()))
     return q, scale

@@ -154,6 +154,10 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
     const int tj = min(tile0 + j / R, ntiles - 1);
     wsv = p.wsf[static_cast<size_t>(tj >> 3) * KS + min(ks0 + j % R, klast)];
   }
+  // The scale loads stay ahead of the weight loads: the LDS store of the
+  // activation scales below waits for them, and with the weight loads issued
+  // first that wait would cover the whole weight stream too.
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. the wave's weight fragments (all R steps of its T tiles) ---------
   // Every weight byte is read by exactly one wave: streaming loads.

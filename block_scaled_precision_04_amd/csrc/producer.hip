@@ -88,12 +88,15 @@ BS_INLINE void unpack8(uint4 v, float* f) {
 // GROUP = true: one scale per 128-wide group of the row instead of one per
 // row; chunk idx = c*256 + t belongs to group idx/16, so the 16 consecutive
 // threads holding a group reduce its maximum with four shuffles.
+// res and rout may be the same buffer (the residual updated in place), so
+// neither is declared __restrict__; every thread reads its chunks of a row
+// before it writes them.
 template <int NC, bool NORM, bool GROUP = false, int T = kThreads>
 __global__ __launch_bounds__(T) void k_row_quant(const uint4* __restrict__ y,
-                                                 const uint4* __restrict__ res,
+                                                 const uint4* res,
                                                  const uint4* __restrict__ gamma, float eps,
                                                  uint2* __restrict__ q, float* __restrict__ scale,
-                                                 uint4* __restrict__ rout, int K) {
+                                                 uint4* rout, int K) {
   static_assert(T % 64 == 0, "whole waves");
   constexpr int kThreads = T;  // threads per row (shadows the file-wide default)
   __shared__ double red_d[T / 64];

@@ -61,3 +61,26 @@ def sample_grid(M, N, nrows, ncols, seed):
     c = np.array(sorted(cols))
     rr, cc = np.meshgrid(r, c, indexing="ij")
     return rr.reshape(-1), cc.reshape(-1)
+
+
+def block_samples(M, N, block, seed):
+    """One random element in every block x block cell of an [M, N] output.
+    Every tile of every tiled launch (256x256 or 128x128 tiles, column strips
+    starting at multiples of 128) contains whole cells, so each tile of each
+    launch is checked at least once."""
+    g = np.random.default_rng(seed)
+    r0, c0 = np.meshgrid(np.arange(0, M, block), np.arange(0, N, block), indexing="ij")
+    r = np.minimum(r0 + g.integers(0, block, r0.shape), M - 1)
+    c = np.minimum(c0 + g.integers(0, block, c0.shape), N - 1)
+    return r.reshape(-1), c.reshape(-1)
+
+
+def oracle_at(fn, rows, cols, *args, chunk=2048):
+    """fn(*args, rows, cols) evaluated in chunks of samples (bounded host
+    memory at K = 17408); returns (c_exact, abs_sum) over all samples."""
+    ce, asum = [], []
+    for i in range(0, len(rows), chunk):
+        _, c, a = fn(*args, rows[i:i + chunk], cols[i:i + chunk])
+        ce.append(c)
+        asum.append(a)
+    return np.concatenate(ce), np.concatenate(asum)

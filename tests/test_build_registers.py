@@ -1,15 +1,27 @@
-"""Every gfx950 kernel of the library fits its register budget: no VGPR/SGPR
-spills and no per-lane scratch.
+"""Checks on the gfx950 assembly of every kernel of the library (hipcc
+cross-compiles without a GPU; each source is compiled once per session).
 
-A spill puts a kernel's registers in scratch memory (private segment) -- an
-extra memory round trip inside loops that are built to keep every operand in
-registers, and a per-dispatch scratch allocation.  The launch bounds and
-occupancy targets of the kernels (e.g. two 256-thread workgroups per CU for
-the 128x128 prefill tile, i.e. at most 256 registers per lane) leave little
-room, so a source change that adds live values (a wider reduction batch, an
-extra fragment set) can tip one over without any test failing on numbers.
-This compiles each source for the device only (hipcc cross-compiles without a
-GPU) and reads the kernel metadata the compiler emits."""
+* Register budget: no VGPR/SGPR spills and no per-lane scratch.  A spill puts
+  a kernel's registers in scratch memory (private segment) -- an extra memory
+  round trip inside loops that are built to keep every operand in registers,
+  and a per-dispatch scratch allocation.  The launch bounds and occupancy
+  targets (e.g. two 256-thread workgroups per CU for the 128x128 prefill
+  tile, i.e. at most 256 registers per lane) leave little room, so a source
+  change that adds live values can tip one over without any test failing on
+  numbers.
+* M0: the direct-to-LDS loads set M0 (the LDS destination base) in inline
+  assembly that lists M0 as clobbered.  The compiler does not preserve a
+  reserved register across such a statement, so the library is correct only
+  while the compiler itself never keeps a value in M0: every write of M0 must
+  be the DMA pattern (s_mov_b32 m0 -> s_nop 0 -> global_load_lds).
+* Decode-kernel load order: each wave issues its activation DMA, then the
+  scale loads, then all of its weight loads, and waits before the first
+  barrier only until the DMA has landed -- at most weight_loads() newer loads
+  may still be outstanding.  If the compiler sinks a scale load below the
+  weight loads, the wait before the LDS store of the scales covers the whole
+  weight stream and the kernel serialises load and compute.
+"""
+import functools
 import glob
 import os
 import re
@@ -21,6 +33,7 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(ROOT, "block_scaled_precision_04_amd", "csrc")
+SOURCES = sorted(os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _hipcc():
@@ -30,18 +43,83 @@ def _hipcc():
     return None
 
 
-@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-@pytest.mark.parametrize("src", sorted(os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip"))))
-def test_no_spills(src, tmp_path):
-    out = tmp_path / (src + ".s")
-    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
-           os.path.join(CSRC, src), "-o", str(out)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-2000:]
-    text = out.read_text()
-    # one metadata block per kernel: .name, then the counts
+pytestmark = pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+
+
+@functools.lru_cache(maxsize=None)
+def _asm(src):
+    """Device assembly of one source, compiled with the library's flags."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, src + ".s")
+        cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+               os.path.join(CSRC, src), "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        with open(out) as f:
+            return f.read()
+
+
+def _kernels(text):
+    """(mangled name, list of instruction lines) per kernel body."""
+    out = []
+    for chunk in re.split(r"\n(?=_Z[^\s:]*:)", text)[1:]:
+        name = chunk.split(":", 1)[0]
+        body = chunk.split("\n")
+        end = next((i for i, ln in enumerate(body) if ln.strip().startswith(".Lfunc_end")), len(body))
+        instrs = []
+        for ln in body[1:end]:
+            s = ln.split(";", 1)[0].strip()
+            if s and not s.startswith(".") and not s.endswith(":"):
+                instrs.append(s)
+        out.append((name, instrs))
+    return out
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_spills(src):
+    text = _asm(src)
     kernels = re.findall(r"\.name:\s+(\S+)", text)
     for key in ("vgpr_spill_count", "sgpr_spill_count", "private_segment_fixed_size"):
         vals = [int(v) for v in re.findall(rf"\.{key}:\s+(\d+)", text)]
         assert all(v == 0 for v in vals), f"{src}: {key} = {vals} (kernels {kernels})"
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_m0_written_only_by_the_dma_pattern(src):
+    for name, ins in _kernels(_asm(src)):
+        for i, s in enumerate(ins):
+            if not re.search(r"\bm0\b", s):
+                continue
+            assert re.fullmatch(r"s_mov_b32\s+m0,\s*s\d+", s), f"{name}: M0 used outside the DMA pattern: {s}"
+            assert i + 2 < len(ins) and ins[i + 1] == "s_nop 0" and ins[i + 2].startswith("global_load_lds_"), \
+                f"{name}: M0 write not followed by s_nop 0 + global_load_lds: {ins[i:i + 3]}"
+
+
+def _vmcnt(s):
+    m = re.search(r"vmcnt\((\d+)\)", s)
+    return int(m.group(1)) if m else None
+
+
+def test_decode_waits_only_for_the_activation_dma():
+    ks = _kernels(_asm("gemm_decode.hip"))
+    seen = 0
+    for name, ins in ks:
+        m = re.search(r"k_decodeILb([01])ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name)
+        if not m:
+            continue
+        mx, mb, tw, kw, t, r = (int(x) for x in m.groups())
+        allowed = t * r + t * ((r + 3) // 4) if mx else 2 * t * r + 1   # weight_loads<MX, T, R>()
+        # block-FP8 also loads its share of the slice's activation scales (kSPer per lane) before them
+        scale_loads = 0 if mx else -(-(kw * r * 16 * mb) // (tw * kw * 64))
+        bar = next(i for i, s in enumerate(ins) if s.startswith("s_barrier"))
+        last_dma = max(i for i, s in enumerate(ins[:bar]) if s.startswith("global_load_lds"))
+        loads_after = sum(1 for s in ins[last_dma + 1:bar] if s.startswith("global_load"))
+        assert loads_after == allowed + scale_loads, \
+            f"{name}: {loads_after} loads after the DMA, expected {allowed + scale_loads}"
+        waits = [_vmcnt(s) for s in ins[last_dma + 1:bar] if s.startswith("s_waitcnt")]
+        waits = [w for w in waits if w is not None]
+        assert waits and min(waits) == allowed, f"{name}: vmcnt waits {waits} before the barrier, want {allowed}"
+        seen += 1
+    assert seen >= 10, f"only {seen} decode instantiations found"

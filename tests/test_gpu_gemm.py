@@ -8,7 +8,7 @@ import block_scaled_precision_04_amd as bs
 from block_scaled_precision_04_amd import synth
 from oracle import gemm, checks
 from tests.gpu_util import (dev_u8, dev_bf16, dev_f32, host_bits16, fp8_block_inputs, w4a8_inputs,
-                            sample_grid)
+                            sample_grid, block_samples, oracle_at)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,12 +130,30 @@ def test_w4a8_full_oracle(M, N, K):
 
 @pytest.mark.parametrize("case", range(len(synth.WORKLOADS[3][1])))
 def test_w4a8_prefill_workload_sampled(case):
+    """Each prefill workload shape: a grid of rows x columns (tile edges,
+    first and last) plus one element in every 128x128 cell, so every output
+    tile of every launch of the tile plan is checked (M=8192 N=34816: all
+    4352 large tiles)."""
     M, N, K = synth.WORKLOADS[3][1][case]
     aq, asc, wp, e = w4a8_inputs(3, case, M, N, K)
     got = host_bits16(_w4_run(aq, asc, wp, e))
     rows, cols = sample_grid(M, N, 20, 40, seed=case)
-    _, ce, asum = gemm.w4a8_mxfp4_gemm_at(aq, asc, wp, e, rows, cols)
+    br, bc = block_samples(M, N, 128, seed=1000 + case)
+    rows, cols = np.r_[rows, br], np.r_[cols, bc]
+    ce, asum = oracle_at(gemm.w4a8_mxfp4_gemm_at, rows, cols, aq, asc, wp, e)
     checks.assert_gemm_close(got[rows, cols], ce, asum, f"w4a8 prefill M={M} N={N} K={K}")
+
+
+def test_w4a8_large_tile_launch_full_oracle():
+    """Every element of one full round of the 256x256 kernel: M = N = 4096,
+    K = 5120 is 16 x 16 = 256 large tiles (one per CU), no column strip, the
+    whole K pipeline (40 steps), against the full fp64 oracle."""
+    M, N, K = 4096, 4096, 5120
+    aq, asc, wp, e = w4a8_inputs(3, 99, M, N, K)
+    assert bs.workspace_bytes(bs.BS_OP_W4A8_MXFP4, M, N, K) == 0      # one unsplit launch
+    got = host_bits16(_w4_run(aq, asc, wp, e))
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(got, ce, asum, f"w4a8 large tiles full M={M} N={N} K={K}")
 
 
 def test_w4a8_down_projection_sampled():
@@ -173,7 +191,9 @@ def test_w4a8_fused_chain():
             checks.assert_gemm_close(ch, ce, asum, "chain decode")
         else:
             rows, cols = sample_grid(M, N, 16, 32, seed=77)
-            _, ce, asum = gemm.w4a8_mxfp4_gemm_at(qo, so, wp, e, rows, cols)
+            br, bc = block_samples(M, N, 128, seed=78)
+            rows, cols = np.r_[rows, br], np.r_[cols, bc]
+            ce, asum = oracle_at(gemm.w4a8_mxfp4_gemm_at, rows, cols, qo, so, wp, e)
             checks.assert_gemm_close(ch[rows, cols], ce, asum, "chain prefill")
 
 
@@ -189,6 +209,70 @@ def test_w4a8_no_out_of_bounds_writes_and_ldc():
     assert np.all(host[mask] == -7.0)
     _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
     checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 strided out")
+
+
+def _guarded(M, N, pad_c=40):
+    """A [M, N] view with leading dimension N + pad_c inside a frame of -7.0
+    (one row above and below, 8 columns left, pad_c - 8 right)."""
+    big = torch.full((M + 2, N + pad_c), -7.0, dtype=torch.bfloat16, device="cuda")
+    return big, big[1:M + 1, 8:8 + N]
+
+
+def _frame_untouched(big, M, N):
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[1:M + 1, 8:8 + N] = False
+    return bool(np.all(host[mask] == -7.0))
+
+
+# decode kernels writing into a strided view inside a guard frame: rows 1..64
+# (one and several 16-row blocks, ragged), K unsplit (few steps) and split
+# across workgroups (the last workgroup of a tile group writes C), and
+# block-FP8 beyond 64 rows (consecutive 64-row launches)
+DECODE_FRAME = [(1, 384), (5, 17408), (16, 640), (17, 5120), (33, 384), (47, 17408), (64, 5120), (100, 2048)]
+
+
+@pytest.mark.parametrize("M,K", DECODE_FRAME)
+def test_fp8_block_decode_strided_out(M, K):
+    N = 1280
+    aq, asc, wq, wsc = fp8_block_inputs(9, 31 * M + K, M, N, K, outliers=True)
+    pre, desc = bs.prelayout_fp8_block(dev_u8(wq))
+    ws = bs.alloc_workspace(bs.BS_OP_FP8_BLOCK, M, N, K)
+    big, view = _guarded(M, N)
+    bs.bsgemm_fp8_block(dev_u8(aq), dev_f32(asc), desc, pre, dev_f32(wsc), out=view, ws=ws)
+    torch.cuda.synchronize()
+    assert _frame_untouched(big, M, N)
+    _, ce, asum = gemm.fp8_block_gemm(aq, asc, wq, wsc)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, f"fp8 decode strided M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,K", [mk for mk in DECODE_FRAME if mk[0] <= 64])
+def test_w4a8_decode_strided_out(M, K):
+    N = 1296
+    aq, asc, wp, e = w4a8_inputs(8, 37 * M + K, M, N, K)
+    big, view = _guarded(M, N)
+    _w4_run(aq, asc, wp, e, out=view)
+    assert _frame_untouched(big, M, N)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, f"w4a8 decode strided M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (8, 256, 2048), (17, 96, 5120), (64, 96, 5120), (40, 48, 384)])
+def test_skinny_guarded_out(M, N, K):
+    """The skinny GEMM takes a dense [M, N] output: written inside a larger
+    buffer, nothing before or after it changes (split and unsplit K)."""
+    g = synth.rng(7 * M + N + K)
+    x = synth.bf16_normal(g, (M, K), 1.0)
+    w = synth.bf16_normal(g, (N, K), 0.02)
+    pad = 256
+    flat = torch.full((M * N + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = flat[pad:pad + M * N].view(M, N)
+    bs.gemm_bf16_skinny(dev_bf16(x), dev_bf16(w), out=out, ws=bs.alloc_workspace(bs.BS_OP_BF16_SKINNY, M, N, K))
+    torch.cuda.synchronize()
+    host = flat.float().cpu().numpy()
+    assert np.all(host[:pad] == -7.0) and np.all(host[pad + M * N:] == -7.0)
+    _, ce, asum = gemm.bf16_gemm(x, w)
+    checks.assert_gemm_close(host_bits16(out), ce, asum, f"skinny guarded M={M} N={N} K={K}")
 
 
 def test_w4a8_large_tiles_strided_out():
