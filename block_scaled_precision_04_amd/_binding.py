@@ -57,6 +57,7 @@ SIGNATURES = {
     "bsgemm_fp8_block": (_I, [_P, _L, _P, _L, _L, _D, _P, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "bsgemm_w4a8_mxfp4": (_I, [_P, _L, _P, _D, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "gemm_bf16_skinny": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
+    "gemm_bf16_skinny_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "add_rms_quant_fp8": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
     "add_rms_quant_fp8_group128": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
     "silu_mul_quant_fp8": (_I, [_P, _P, _P, _I, _I, _P]),
@@ -276,6 +277,25 @@ def gemm_bf16_skinny(x, w, out=None, ws=None):
     w = w.contiguous()
     ws_p, ws_n = _ws(fn, ws)
     _check(fn, lib().gemm_bf16_skinny(_ptr(x), _ptr(w), _ptr(out), M, N, K, ws_p, ws_n, _stream()))
+    return out
+
+
+def gemm_bf16_skinny_noalloc(x, w, out=None):
+    """gemm_bf16_skinny without a workspace: the library keeps the split-K
+    scratch in a static per-GPU array (calls that overlap on one GPU race).
+    The C call allocates nothing; pass `out` to allocate nothing here either."""
+    fn = "gemm_bf16_skinny_noalloc"
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2 and isinstance(w, torch.Tensor) and w.dim() == 2, fn,
+          "x [M, K] and w [N, K] must be 2-D tensors")
+    M, K = x.shape
+    N = w.shape[0]
+    _arg(fn, "x", x, (M, K), _BF16, contiguous=True)
+    _arg(fn, "w", w, (N, K), _BF16, contiguous=True)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _arg(fn, "out", out, (M, N), _BF16, contiguous=True)
+    _on_device(fn, x, w, out)
+    _check(fn, lib().gemm_bf16_skinny_noalloc(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream()))
     return out
 
 

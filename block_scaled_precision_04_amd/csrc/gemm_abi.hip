@@ -46,6 +46,7 @@ BS_API const char* bs_status_string(int status) {
     case BS_ERR_WORKSPACE: return "workspace missing or too small";
     case BS_ERR_LAUNCH: return "kernel launch failed";
     case BS_ERR_ARG: return "invalid argument";
+    case BS_ERR_SCRATCH: return "shape needs more than the static scratch array";
     default: return "unknown status";
   }
 }

@@ -19,6 +19,8 @@
 // fence writes back and invalidates the L2 of the XCD on every workgroup).
 // Rows past M load row M-1 (unconditional loads) and only ever reach output
 // columns that are not stored.
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -137,4 +139,69 @@ int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, i
   else if (M <= 32) k_skinny<2><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);
   else k_skinny<4><<<grid, 256, 0, st>>>(x, w, c, M, N, K, slab, counters);
   return bs_launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// The same GEMM for callers that cannot allocate: its split-K scratch is a
+// static device array instead of a caller workspace.  Each GPU the library
+// runs on holds its own copy of the array (zero-filled when the code object
+// is loaded) until the process ends.  In host code `scratch` names a host-side
+// stand-in, not a device address: the device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and only that
+// pointer is handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = BS_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kWsCounterBytes && kScratchBytes % 256 == 0, "scratch layout");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void k_zero_words(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// The device address of `scratch` on the device of stream st (which must be
+// the current device).  The first call on a device looks it up and clears
+// the counter region with a kernel on st (a kernel rather than a memset, so
+// that the clear is also valid if it lands inside a captured graph).
+int scratch_for(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BS_ERR_ARG;
+  if (st != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return BS_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return BS_ERR_LAUNCH;
+    constexpr int kWords = static_cast<int>(kWsCounterBytes / sizeof(int));
+    k_zero_words<<<(kWords + 255) / 256, 256, 0, st>>>(static_cast<int*>(ptr), kWords);
+    if (hipGetLastError() != hipSuccess) return BS_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BS_OK;
+}
+}  // namespace
+
+extern "C" BS_API int gemm_bf16_skinny_noalloc(const void* x, const void* w, void* c, int M, int N, int K,
+                                               bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
+  BS_CHECK(x && w && c, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && M <= 64 && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(x, 16) && bs_aligned(w, 16) && bs_aligned(c, 4), BS_ERR_ALIGN);
+  const size_t need = bs_skinny_workspace(M, N, K);
+  BS_CHECK(need <= kScratchBytes, BS_ERR_SCRATCH);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_for(st, &ws);
+    if (rc != BS_OK) return rc;
+  }
+  return bs_launch_skinny(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                          static_cast<uint16_t*>(c), M, N, K, ws, st);
 }

@@ -55,7 +55,8 @@ enum {
   BS_ERR_LAYOUT = -4,    /* weight descriptor does not match the call          */
   BS_ERR_WORKSPACE = -5, /* workspace missing or smaller than required         */
   BS_ERR_LAUNCH = -6,    /* the HIP runtime refused a launch                   */
-  BS_ERR_ARG = -7        /* any other invalid argument                         */
+  BS_ERR_ARG = -7,       /* any other invalid argument                         */
+  BS_ERR_SCRATCH = -8    /* the shape needs more than the static scratch array */
 };
 
 /* Human-readable name of a status code (static string). */
@@ -190,6 +191,27 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
  * across workgroups; ws must hold bs_workspace_bytes(BS_OP_BF16_SKINNY,...). */
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws,
                             size_t ws_bytes, bs_stream_t stream);
+
+/* The skinny GEMM for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and result as gemm_bf16_skinny, without a workspace.  Its split-K
+ * scratch (counters and partials) is a static device array of
+ * BS_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends; the call itself allocates and frees nothing.
+ *   - A shape whose split-K scratch, bs_workspace_bytes(BS_OP_BF16_SKINNY,
+ *     M, N, K), exceeds BS_NOALLOC_SCRATCH_BYTES returns BS_ERR_SCRATCH and
+ *     launches nothing (e.g. at M = 64: N <= 1600 for K = 5120, N <= 4032 for
+ *     K = 2048).
+ *   - The stream must belong to the current device (else BS_ERR_ARG).
+ *   - The first call on a device looks up the array's address on that device
+ *     and clears its counters with a kernel on the stream; make it outside
+ *     graph capture.  After that every call leaves the counters zeroed.
+ *   - All calls on one GPU share that GPU's array: calls ordered on one stream
+ *     are safe, calls that may overlap in time on one GPU (several streams,
+ *     several host threads) race and give undefined results. */
+#define BS_NOALLOC_SCRATCH_BYTES (4u << 20)
+BS_API int gemm_bf16_skinny_noalloc(const void* x, const void* w, void* c, int M, int N, int K,
+                                    bs_stream_t stream);
 
 /* ----------------------------------------------------------- producers */
 
