@@ -30,6 +30,15 @@ def build(verbose=False):
         raise RuntimeError("libbsgemm build failed:\n" + out)
     if verbose and out.strip():
         print(out)
+    else:
+        # one line per distinct compiler warning, always reported.  The known
+        # one is the M0 clobber of the direct-to-LDS loads' inline assembly:
+        # the compiler does not preserve M0 across them, which is safe only
+        # while it keeps no value of its own in M0 (checked by the assembly
+        # scan in tests/test_build_registers.py).
+        seen = sorted({l.split("warning:", 1)[1].strip() for l in out.splitlines() if "warning:" in l})
+        for w in seen:
+            print(f"libbsgemm build warning: {w}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -93,8 +93,16 @@ constexpr int weight_loads() {
 // LDS: the activation slice (KW*R steps x rs rows x 128 B, as 16-byte chunks)
 // and, for block-FP8, its scales [KW*R][rs]; the cross-wave partials reuse the
 // slice after the MFMAs.
+// At most 256 threads per workgroup (one wave per SIMD) give the compiler a
+// 512-register budget, and it then accumulates the 16x16x128 scaled MFMA in
+// the accumulator registers (AGPRs).  The one decode configuration ever built
+// that way (MXFP4, TW=2 KW=2 T=1 R=8) gave wrong results on the GPU although
+// its indexing is exact and the compiler's wait states before reading the
+// AGPRs follow the 8-pass rules; every configuration in use accumulates in
+// ordinary VGPRs.  So that form is kept out of this kernel.
 template <bool MX, int MB, int TW, int KW, int T, int R>
 __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
+  static_assert(TW * KW > 4, "<= 4 waves per workgroup puts the accumulators in AGPRs (see above)");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int last;
   constexpr int kThreads = TW * KW * 64;

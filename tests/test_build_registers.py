@@ -14,6 +14,12 @@ cross-compiles without a GPU; each source is compiled once per session).
   reserved register across such a statement, so the library is correct only
   while the compiler itself never keeps a value in M0: every write of M0 must
   be the DMA pattern (s_mov_b32 m0 -> s_nop 0 -> global_load_lds).
+* Scaled 16x16x128 MFMA accumulating in AGPRs: the one kernel ever built that
+  way (an MXFP4 decode configuration with four waves, whose small register
+  demand per workgroup let the compiler keep the accumulator in AGPRs) gave
+  wrong results on the GPU, with exact indexing and the compiler's documented
+  wait states in place; every kernel in use writes that MFMA's result to
+  ordinary VGPRs, and this scan keeps it so.
 * Decode-kernel load order: each wave issues its activation DMA, then the
   scale loads, then all of its weight loads, and waits before the first
   barrier only until the DMA has landed -- at most weight_loads() newer loads
@@ -123,3 +129,12 @@ def test_decode_waits_only_for_the_activation_dma():
         assert waits and min(waits) == allowed, f"{name}: vmcnt waits {waits} before the barrier, want {allowed}"
         seen += 1
     assert seen >= 10, f"only {seen} decode instantiations found"
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_scaled_16x16x128_mfma_accumulates_in_vgprs(src):
+    for name, ins in _kernels(_asm(src)):
+        for s in ins:
+            if s.startswith("v_mfma_scale_f32_16x16x128_f8f6f4"):
+                dst = s.split()[1]
+                assert dst.startswith("v["), f"{name}: scaled 16x16x128 MFMA writes {dst}: {s}"
