@@ -28,10 +28,24 @@ MXFP4 e8m0 scales (uint8 [N, K/32]):
     with ks = k32//4, lane = n%16 + 16*(k32%4), KQ = ceil(KS/4);
   i.e. one dword per lane holds the scales of four consecutive K steps.
   Bytes of a final, partly used dword are 0x7F (scale 1.0, never read).
+
+Activation-tiled producer output (e4m3 codes [M, K], K % 128 == 0): the
+A-fragment order of gfx950's 32x32x64 MFMA with an 8-bit operand, whose lane
+l holds row l % 32 and, of each 64-wide half of a 128-K step, the K values
+16*(l//32) .. +15 in bytes 0..15 and 32 + 16*(l//32) .. +15 in bytes 16..31.
+Rows are padded to a multiple of 32:
+    A[m, k] goes to byte  ((rb*KS + ks)*2 + h)*2048 + lane*32 + c*16 + j
+    with rb = m//32, ks = k//128, h = (k%128)//64, k' = k%64 = 32c + 16g + j,
+         lane = m%32 + 32g;
+  i.e. each (32-row block, 128-K step) is 4 KiB: two 2 KiB halves, each the
+  32 bytes of every lane of one MFMA operand (radiance_mxfp4.py page, the
+  A_TILED_MIN_M comment: the producer writes fragment-tiled activations with
+  rows padded, so the consumer reads fragments without re-laying them out).
 """
 import numpy as np
 
 E8M0_PAD = 0x7F
+A_TILE_ROWS = 32
 
 
 def prelayout_fp8_block(w):
@@ -91,3 +105,29 @@ def unprelayout_mxfp4_scales(pre, N, K):
     t = np.asarray(pre, np.uint8).reshape(nt, KQ, 4, 16, 4)       # [nt][kq][g][row][r]
     full = np.ascontiguousarray(t.transpose(0, 3, 1, 4, 2)).reshape(N, KQ * 16)
     return full[:, : K // 32].copy()
+
+
+def tiled_activation_bytes(M, K):
+    return -(-M // A_TILE_ROWS) * A_TILE_ROWS * K
+
+
+def tile_activation(q):
+    """[M, K] e4m3 codes -> the activation-tiled byte order (pad rows are 0)."""
+    q = np.asarray(q, np.uint8)
+    M, K = q.shape
+    assert K % 128 == 0
+    Mp = -(-M // A_TILE_ROWS) * A_TILE_ROWS
+    padded = np.zeros((Mp, K), np.uint8)
+    padded[:M] = q
+    RB, KS = Mp // 32, K // 128
+    # [rb][r][ks][h][c][g][j] -> [rb][ks][h][g][r][c][j]; lane = r + 32 g
+    t = padded.reshape(RB, 32, KS, 2, 2, 2, 16).transpose(0, 2, 3, 5, 1, 4, 6)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def untile_activation(t, M, K):
+    """Inverse of tile_activation: the first M rows back in row-major order."""
+    Mp = -(-M // A_TILE_ROWS) * A_TILE_ROWS
+    RB, KS = Mp // 32, K // 128
+    a = np.asarray(t, np.uint8)[: Mp * K].reshape(RB, KS, 2, 2, 32, 2, 16)   # [rb][ks][h][g][r][c][j]
+    return np.ascontiguousarray(a.transpose(0, 4, 1, 2, 5, 3, 6)).reshape(Mp, K)[:M].copy()

@@ -52,3 +52,28 @@ def test_mxfp4_layout_roundtrip_and_formula():
                 ks = k32 // 4
                 used[(((n // 16) * KQ + ks // 4) * 64 + n % 16 + 16 * (k32 % 4)) * 4 + ks % 4] = True
         assert np.all(ps[~used] == layout.E8M0_PAD)
+
+
+def test_activation_tiling_roundtrip_and_operand_order():
+    """The activation-tiled order against the 32x32x64 MFMA 8-bit operand
+    order read lane by lane (row l % 32; bytes 0..15 hold K = 16*(l//32)+b
+    and bytes 16..31 K = 32 + 16*(l//32) + b - 16 of each 64-wide half):
+    every byte of the tiled buffer is found at the (row, K) that order names."""
+    g = np.random.default_rng(32)
+    for M, K in [(32, 128), (45, 384), (70, 256)]:
+        q = g.integers(0, 256, (M, K), dtype=np.uint8)
+        t = layout.tile_activation(q)
+        Mp = -(-M // 32) * 32
+        assert t.size == layout.tiled_activation_bytes(M, K) == Mp * K
+        assert np.array_equal(layout.untile_activation(t, M, K), q)
+        KS = K // 128
+        for rb in range(Mp // 32):
+            for ks in range(KS):
+                for h in range(2):
+                    base = ((rb * KS + ks) * 2 + h) * 2048
+                    for lane in range(64):
+                        m = 32 * rb + lane % 32
+                        for b in range(32):
+                            kk = 16 * (lane // 32) + b if b < 16 else 32 + 16 * (lane // 32) + b - 16
+                            want = q[m, 128 * ks + 64 * h + kk] if m < M else 0
+                            assert t[base + lane * 32 + b] == want
