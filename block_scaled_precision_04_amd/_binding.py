@@ -56,10 +56,12 @@ SIGNATURES = {
     "bs_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "bsgemm_fp8_block": (_I, [_P, _L, _P, _L, _L, _D, _P, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "bsgemm_w4a8_mxfp4": (_I, [_P, _L, _P, _D, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
+    "bsgemm_w4a8_mxfp4_atiled": (_I, [_P, _P, _D, _P, _P, _L, _I, _I, _I, _P, _Z, _P]),
     "gemm_bf16_skinny": (_I, [_P, _P, _P, _I, _I, _I, _P, _Z, _P]),
     "gemm_bf16_skinny_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "add_rms_quant_fp8": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
     "add_rms_quant_fp8_group128": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
+    "add_rms_quant_fp8_tiled": (_I, [_P, _P, _P, _F, _P, _P, _P, _I, _I, _P]),
     "silu_mul_quant_fp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_per_token": (_I, [_P, _P, _P, _I, _I, _P]),
     "quant_fp8_group128": (_I, [_P, _P, _P, _I, _I, _P]),
@@ -260,6 +262,33 @@ def bsgemm_w4a8_mxfp4(a, a_scale, desc, w_pre, out=None, ws=None):
     return out
 
 
+def tiled_activation_bytes(M, K):
+    """Bytes of an activation-tiled [M, K] e4m3 buffer (rows padded to 32)."""
+    return (M + 31) // 32 * 32 * K
+
+
+def bsgemm_w4a8_mxfp4_atiled(a_tiled, a_scale, desc, w_pre, M, out=None, ws=None):
+    """C[M,N] bf16 = MXFP4 W4A8 GEMM on an activation in the activation-tiled
+    order (uint8, tiled_activation_bytes(M, K) bytes, from
+    add_rms_quant_fp8_tiled); M > 64."""
+    fn = "bsgemm_w4a8_mxfp4_atiled"
+    N, K = desc.N, desc.K
+    _arg(fn, "a_tiled", a_tiled, (tiled_activation_bytes(M, K),), _FP8, contiguous=True)
+    _arg(fn, "a_scale", a_scale, (M,), (torch.float32,), unit_inner=False)
+    _arg(fn, "w_pre", w_pre, (w_pre.numel(),), (torch.uint8,), contiguous=True)
+    _need(w_pre.numel() >= desc.total_bytes, fn, f"w_pre holds {w_pre.numel()} bytes, the layout needs "
+                                                 f"{desc.total_bytes}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_tiled.device)
+    _arg(fn, "out", out, (M, N), _BF16)
+    _on_device(fn, a_tiled, a_scale, w_pre, out, ws)
+    ws_p, ws_n = _ws(fn, ws)
+    _check(fn, lib().bsgemm_w4a8_mxfp4_atiled(
+        _ptr(a_tiled), _ptr(a_scale.contiguous()), ctypes.byref(desc), _ptr(w_pre), _ptr(out), out.stride(0),
+        M, N, K, ws_p, ws_n, _stream()))
+    return out
+
+
 def gemm_bf16_skinny(x, w, out=None, ws=None):
     """C[M,N] bf16 = x[M,K] . w[N,K]^T (M <= 64).  ws: from alloc_workspace when K is split."""
     fn = "gemm_bf16_skinny"
@@ -337,6 +366,23 @@ def add_rms_quant_fp8(y, residual, gamma, eps=1e-6, q=None, scale=None, residual
     y, residual, gamma, q, scale, residual_out = _producer_args(fn, y, residual, gamma, q, scale, residual_out, 1)
     M, K = y.shape
     _check(fn, lib().add_rms_quant_fp8(
+        _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
+        M, K, _stream()))
+    return q, scale, residual_out
+
+
+def add_rms_quant_fp8_tiled(y, residual, gamma, eps=1e-6, q=None, scale=None, residual_out=None):
+    """(q e4m3 in the activation-tiled order, uint8 [tiled_activation_bytes(M, K)],
+    scale fp32 [M], residual_out bf16 [M,K])."""
+    fn = "add_rms_quant_fp8_tiled"
+    _need(isinstance(y, torch.Tensor) and y.dim() == 2, fn, "y must be a 2-D tensor [M, K]")
+    M, K = y.shape
+    if q is None:
+        q = torch.empty((tiled_activation_bytes(M, K),), dtype=torch.uint8, device=y.device)
+    _arg(fn, "q", q, (tiled_activation_bytes(M, K),), _FP8, contiguous=True)
+    q2 = q.view(-1)[: M * K].view(M, K)      # shape stand-in for the shared checks only
+    y, residual, gamma, _, scale, residual_out = _producer_args(fn, y, residual, gamma, q2, scale, residual_out, 1)
+    _check(fn, lib().add_rms_quant_fp8_tiled(
         _ptr(y), _ptr(residual), _ptr(gamma), ctypes.c_float(eps), _ptr(q), _ptr(scale), _ptr(residual_out),
         M, K, _stream()))
     return q, scale, residual_out

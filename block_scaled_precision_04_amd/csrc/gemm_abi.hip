@@ -14,7 +14,7 @@ int bs_launch_fp8_block_prefill(const uint8_t* a, int64_t lda, const float* as, 
                                 hipStream_t st);
 int bs_fp8_prefill_min_m();
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, hipStream_t st);
+                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, bool a_tiled, hipStream_t st);
 size_t bs_prefill_workspace(int M, int N, int K);
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
                      hipStream_t st);
@@ -130,7 +130,32 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
   const int wst = check_workspace(bs_prefill_workspace(M, N, K), ws, ws_bytes);
   if (wst != BS_OK) return wst;
   return bs_launch_w4a8_prefill(static_cast<const uint8_t*>(a), lda, a_scale, w, wsc, static_cast<uint16_t*>(c),
-                                ldc, M, N, K, ws, st);
+                                ldc, M, N, K, ws, false, st);
+}
+
+BS_API int bsgemm_w4a8_mxfp4_atiled(const void* a_tiled, const float* a_scale, const bs_wdesc* wd, const void* w_pre,
+                                    void* c, int64_t ldc, int M, int N, int K, void* ws, size_t ws_bytes,
+                                    bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
+  BS_CHECK(a_tiled && a_scale && wd && w_pre && c, BS_ERR_NULL);
+  BS_CHECK(M > kW4A8DecodeMaxM && M <= (1 << 22) && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0,
+           BS_ERR_SHAPE);
+  BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_MXFP4 && wd->N == N && wd->K == K &&
+               wd->scales_offset % 256 == 0 && wd->scales_offset >= wd->codes_bytes,
+           BS_ERR_LAYOUT);
+  BS_CHECK(ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
+  BS_CHECK(bs_aligned(a_tiled, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
+           BS_ERR_ALIGN);
+  // the tiled activation (rows padded to 32) and the weight codes are
+  // addressed with unsigned 32-bit offsets
+  BS_CHECK(static_cast<uint64_t>((M + 31) / 32) * 32 * static_cast<uint64_t>(K) < (1ull << 32), BS_ERR_SHAPE);
+  BS_CHECK(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) / 2 < (1ull << 32), BS_ERR_SHAPE);
+  const int wst = check_workspace(bs_prefill_workspace(M, N, K), ws, ws_bytes);
+  if (wst != BS_OK) return wst;
+  const uint8_t* w = static_cast<const uint8_t*>(w_pre);
+  return bs_launch_w4a8_prefill(static_cast<const uint8_t*>(a_tiled), K, a_scale, w,
+                                reinterpret_cast<const uint32_t*>(w + wd->scales_offset), static_cast<uint16_t*>(c),
+                                ldc, M, N, K, ws, true, static_cast<hipStream_t>(stream));
 }
 
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws, size_t ws_bytes,

@@ -72,7 +72,12 @@ struct PrefillCfg {
 // grid (tiles, S): workgroup (x, y) computes tile x over the y-th of S equal
 // runs of K steps; with S > 1 the partial tile goes to the workspace slab and
 // the last of the S workgroups of a tile adds them in split order.
-template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL>
+// AT = true: the activation arrives in the activation-tiled order (32-row
+// blocks of 4 KiB per K step, each half step the 32 bytes of every lane of
+// one 32x32x64 MFMA operand, written so by the tiled producer).  A stage's
+// activation tile is then BM/32 contiguous 4 KiB blocks, copied as they are,
+// and a fragment is read at a fixed lane offset: no swizzle, no re-layout.
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT = false>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m,
@@ -105,9 +110,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll
   for (int i = 0; i < C::kAIters; ++i) {
     const int p = (i * C::kWaves + wave) * 64 + l;  // 16-byte position in the activation stage
-    const int row = p >> 3, slot = p & 7;
-    aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(lda) +
-              static_cast<uint32_t>(16 * swz(row, slot));
+    if constexpr (AT) {
+      // tiled: position p is byte 16 (p % 256) of the stage's (p / 256)-th
+      // 32-row block; blocks past the padded M re-read the last one
+      const int rb = min((m0 >> 5) + (p >> 8), ((M + 31) >> 5) - 1);
+      aoff[i] = static_cast<uint32_t>(rb) * static_cast<uint32_t>(KS) * 4096u + static_cast<uint32_t>((p & 255) * 16);
+    } else {
+      const int row = p >> 3, slot = p & 7;
+      aoff[i] = static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(lda) +
+                static_cast<uint32_t>(16 * swz(row, slot));
+    }
   }
   uint32_t boff_g[C::kBIters];
 #pragma unroll
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   auto dma_one = [&](int i, int ks, int buf) {
     const uint32_t base = lds0 + buf * C::kStage;
     if (i < C::kAIters) {
-      dma16(base + (i * C::kWaves + wave) * 1024, a + ks * 128, aoff[i]);
+      dma16(base + (i * C::kWaves + wave) * 1024, a + static_cast<size_t>(ks) * (AT ? 4096 : 128), aoff[i]);
     } else if (i < C::kAIters + C::kBIters) {
       const int j = i - C::kAIters;
       dma16(base + C::kAStage + (j * C::kWaves + wave) * 1024, w + static_cast<size_t>(ks) * 1024, boff_g[j]);
@@ -159,6 +171,23 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll
   for (int q = 0; q < C::kTM; ++q) arow[q] = wm * (BM / WM) + 32 * q + (l & 31);
 
+  // the activation fragment of 32-row sub-tile q, half step hh, from stage st
+  auto a_frag = [&](const uint8_t* st, int hh, int q) {
+    uint4 u, v;
+    if constexpr (AT) {
+      // the lane's 32 bytes of the sub-tile's block, as the producer laid them out
+      const uint8_t* src = st + (arow[q] >> 5) * 4096 + hh * 2048 + l * 32;
+      u = *reinterpret_cast<const uint4*>(src);
+      v = *reinterpret_cast<const uint4*>(src + 16);
+    } else {
+      // chunks 4hh + g and 4hh + 2 + g of the row (the 8-bit operand's order)
+      const int r = arow[q];
+      const int c0 = 4 * hh + (l >> 5);
+      u = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0));
+      v = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0 + 2));
+    }
+    return v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  };
   // fragments of one half step (64 K): weight, activation, e8m0 dword per p
   struct Frag {
     v8i b[C::kTN];
@@ -173,14 +202,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       f.s[p] = *reinterpret_cast<const uint32_t*>(st + soff[p][hh]);
     }
 #pragma unroll
-    for (int q = 0; q < C::kTM; ++q) {
-      // chunks 4hh + g and 4hh + 2 + g of the row (the 8-bit operand's order)
-      const int r = arow[q];
-      const int c0 = 4 * hh + (l >> 5);
-      const uint4 u = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0));
-      const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0 + 2));
-      f.a[q] = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
-    }
+    for (int q = 0; q < C::kTM; ++q) f.a[q] = a_frag(st, hh, q);
   };
   // MFMAs of one half step; with dks >= 0 the loads of step dks (into buffer
   // dbuf) are issued between them (one after each MFMA), so the load unit is
@@ -215,12 +237,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       f.b[p] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       f.s[p] = *reinterpret_cast<const uint32_t*>(st + soff[p][hh]);
     } else {
-      const int q = i - C::kTN;
-      const int r = arow[q];
-      const int c0 = 4 * hh + (l >> 5);
-      const uint4 u = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0));
-      const uint4 v = *reinterpret_cast<const uint4*>(st + r * 128 + 16 * swz(r, c0 + 2));
-      f.a[q] = v8i{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      f.a[i - C::kTN] = a_frag(st, hh, i - C::kTN);
     }
   };
   // MFMAs of one half step; after MFMA i, DMA i of step dks (if dks >= 0)
@@ -419,7 +436,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL>
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT>
 int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint8_t* wsc, uint16_t* c,
                int64_t ldc, int M, int N, int KS, int group_m, int S, void* ws, hipStream_t st) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -430,7 +447,7 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
     counters = static_cast<int*>(ws);
     slab = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
-  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
+  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL, AT><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
       a, static_cast<int>(lda), as, w, wsc, c, ldc, M, N, KS, group_m, slab, counters);
   return bs_launch_status();
 }
@@ -498,14 +515,17 @@ size_t bs_prefill_workspace(int M, int N, int K) {
   return kWsCounterBytes + static_cast<size_t>(pl.s) * pl.tiles * 128 * 128 * sizeof(float);
 }
 
-int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
-                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
+namespace {
+// The tile plan's launches; a_tiled selects the activation-tiled input order.
+template <bool AT>
+int launch_plan(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc, uint16_t* c,
+                int64_t ldc, int M, int N, int K, void* ws, hipStream_t st) {
   const int KS = K / 128;
   const uint8_t* sc = reinterpret_cast<const uint8_t*>(wsc);
   const PrefillPlan pl = prefill_plan(M, N, K);
   if (pl.n_main > 0) {
-    const int rc = launch_cfg<256, 256, 2, 2, 1, false, true>(a, lda, as, w, sc, c, ldc, M, pl.n_main, KS, 4, 1,
-                                                               nullptr, st);
+    const int rc = launch_cfg<256, 256, 2, 2, 1, false, true, AT>(a, lda, as, w, sc, c, ldc, M, pl.n_main, KS, 4, 1,
+                                                                   nullptr, st);
     if (rc != BS_OK || pl.tiles == 0) return rc;
   }
   // a small-tile launch over columns [n0, n1): the weight's n-tiles from
@@ -513,13 +533,20 @@ int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const
   // 16-column tile), output columns from n0 on
   auto small = [&](int n0, int n1, int s, void* work) {
     const size_t nt_off = static_cast<size_t>(n0) / 16;
-    return launch_cfg<128, 128, 2, 2, 2, true, false>(a, lda, as, w + nt_off * KS * 1024,
-                                                      sc + nt_off * ((KS + 3) / 4) * 256, c + n0, ldc, M, n1 - n0,
-                                                      KS, 4, s, work, st);
+    return launch_cfg<128, 128, 2, 2, 2, true, false, AT>(a, lda, as, w + nt_off * KS * 1024,
+                                                          sc + nt_off * ((KS + 3) / 4) * 256, c + n0, ldc, M, n1 - n0,
+                                                          KS, 4, s, work, st);
   };
   if (pl.n_mid > pl.n_main) {
     const int rc = small(pl.n_main, pl.n_mid, 1, nullptr);
     if (rc != BS_OK || pl.tiles == 0) return rc;
   }
   return small(pl.n_mid, N, pl.s, ws);
+}
+}  // namespace
+
+int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
+                           uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, bool a_tiled, hipStream_t st) {
+  return a_tiled ? launch_plan<true>(a, lda, as, w, wsc, c, ldc, M, N, K, ws, st)
+                 : launch_plan<false>(a, lda, as, w, wsc, c, ldc, M, N, K, ws, st);
 }

@@ -77,6 +77,19 @@ BS_INLINE uint2 quant8(const float* h, float s) {
   return make_uint2(lo, hi);
 }
 
+// Activation-tiled order (the radiance_mxfp4.py page's fragment-tiled
+// producer output, A_TILED_MIN_M comment, laid out for gfx950): the operand
+// order of the 32x32x64 MFMA with an 8-bit operand, rows in blocks of 32.
+// A (32-row block, 128-K step) is 4 KiB, two 2 KiB halves of 64 K; in a half,
+// lane l holds row l % 32 and 32 bytes: K = 16*(l/32) .. +15, then
+// 32 + 16*(l/32) .. +15.  Byte offset of codes (m, k .. k+7), k % 8 == 0:
+BS_INLINE size_t tiled_offset(int m, int k, int KS) {
+  const int kp = k & 63;
+  const int lane = (m & 31) + 32 * ((kp >> 4) & 1);
+  return ((static_cast<size_t>(m >> 5) * KS + (k >> 7)) * 2 + ((k >> 6) & 1)) * 2048 + lane * 32 + (kp >> 5) * 16 +
+         (kp & 15);
+}
+
 BS_INLINE void unpack8(uint4 v, float* f) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
   f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
@@ -88,10 +101,12 @@ BS_INLINE void unpack8(uint4 v, float* f) {
 // GROUP = true: one scale per 128-wide group of the row instead of one per
 // row; chunk idx = c*256 + t belongs to group idx/16, so the 16 consecutive
 // threads holding a group reduce its maximum with four shuffles.
+// TILED = true: the codes go out in the activation-tiled order (below)
+// instead of row-major [M, K].
 // res and rout may be the same buffer (the residual updated in place), so
 // neither is declared __restrict__; every thread reads its chunks of a row
 // before it writes them.
-template <int NC, bool NORM, bool GROUP = false, int T = kThreads>
+template <int NC, bool NORM, bool GROUP = false, int T = kThreads, bool TILED = false>
 __global__ __launch_bounds__(T) void k_row_quant(const uint4* __restrict__ y,
                                                  const uint4* res,
                                                  const uint4* __restrict__ gamma, float eps,
@@ -188,7 +203,11 @@ __global__ __launch_bounds__(T) void k_row_quant(const uint4* __restrict__ y,
       const int idx = c * kThreads + t;
       if (idx < nch) {
         const uint2 v = quant8(h[c], s);
-        st_stream8(q + base + idx, v.x, v.y);
+        if constexpr (TILED)
+          st_stream8(reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(q) + tiled_offset(row, idx * 8, K >> 7)),
+                     v.x, v.y);
+        else
+          st_stream8(q + base + idx, v.x, v.y);
       }
     }
   }
@@ -339,13 +358,13 @@ int launch_silu_quant(const void* gu, void* q, float* scale, int M, int N, hipSt
 // 128-thread rows of up to five chunks per thread, which keep more rows in
 // flight per CU (M = 8192, K = 5120: 63 -> 56 us, graph-replayed over inputs
 // pooled past the Infinity Cache).
-template <bool NORM, bool GROUP = false>
+template <bool NORM, bool GROUP = false, bool TILED = false>
 int launch_row_quant(const void* y, const void* res, const void* gamma, float eps, void* q, float* scale,
                      void* rout, int M, int K, hipStream_t st) {
   if (M >= 2048 && K <= 5120) {
     const int nc = (K / 8 + 127) / 128;
 #define BS_ROWQ128(N_)                                                                                  \
-  k_row_quant<N_, NORM, GROUP, 128><<<dim3(M), dim3(128), 0, st>>>(                                    \
+  k_row_quant<N_, NORM, GROUP, 128, TILED><<<dim3(M), dim3(128), 0, st>>>(                             \
       static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
       static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
     if (nc <= 1) BS_ROWQ128(1);
@@ -359,7 +378,7 @@ int launch_row_quant(const void* y, const void* res, const void* gamma, float ep
   const int nc = (K / 8 + kThreads - 1) / kThreads;
   dim3 grid(M), block(kThreads);
 #define BS_ROWQ(N_)                                                                                    \
-  k_row_quant<N_, NORM, GROUP><<<grid, block, 0, st>>>(                                                 \
+  k_row_quant<N_, NORM, GROUP, kThreads, TILED><<<grid, block, 0, st>>>(                                \
       static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
       static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
   if (nc <= 1) BS_ROWQ(1);
@@ -391,6 +410,19 @@ BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* ga
   BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
   return launch_row_quant<true>(y, residual, gamma, eps, q, scale, residual_out, M, K,
                                 static_cast<hipStream_t>(stream));
+}
+
+BS_API int add_rms_quant_fp8_tiled(const void* y, const void* residual, const void* gamma, float eps, void* q_tiled,
+                                   float* scale, void* residual_out, int M, int K, bs_stream_t stream) {
+  if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
+  BS_CHECK(y && residual && gamma && q_tiled && scale && residual_out, BS_ERR_NULL);
+  BS_CHECK(M >= 1 && K >= 128 && K % 128 == 0 && K <= kMaxRowK, BS_ERR_SHAPE);
+  BS_CHECK(bs_aligned(y, 16) && bs_aligned(residual, 16) && bs_aligned(gamma, 16) && bs_aligned(q_tiled, 16) &&
+               bs_aligned(scale, 4) && bs_aligned(residual_out, 16),
+           BS_ERR_ALIGN);
+  BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
+  return launch_row_quant<true, false, true>(y, residual, gamma, eps, q_tiled, scale, residual_out, M, K,
+                                             static_cast<hipStream_t>(stream));
 }
 
 BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const void* gamma, float eps, void* q,

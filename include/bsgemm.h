@@ -184,6 +184,22 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
                              const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
                              size_t ws_bytes, bs_stream_t stream);
 
+/* The same GEMM on an activation in the activation-tiled order written by
+ * add_rms_quant_fp8_tiled (radiance_mxfp4.py page, the A_TILED_MIN_M comment:
+ * at large M the producer emits fragment-tiled activations and the consumer
+ * takes them without re-laying them out).  The order is that of gfx950's
+ * 32x32x64 MFMA operand with 8-bit data, rows in blocks of 32: a (32-row
+ * block rb, 128-K step ks) is the 4 KiB at byte ((rb*K/128 + ks)*4096); in
+ * its half h (2 KiB at +2048h), lane l's 32 bytes (at +32l) hold row
+ * 32rb + l%32, K = 128ks + 64h + 16(l/32) .. +15, then 128ks + 64h + 32 +
+ * 16(l/32) .. +15.  a_tiled holds ceil(M/32)*32*K bytes; the codes of the pad
+ * rows are never used.  Prefill regime only: M > 64 (smaller M is the decode
+ * kernel's row-major input).  Other arguments, the workspace and the result
+ * as bsgemm_w4a8_mxfp4; needs ceil(M/32)*32*K < 2^32. */
+BS_API int bsgemm_w4a8_mxfp4_atiled(const void* a_tiled, const float* a_scale, const bs_wdesc* wd,
+                                    const void* w_pre, void* c, int64_t ldc, int M, int N, int K, void* ws,
+                                    size_t ws_bytes, bs_stream_t stream);
+
 /* Skinny bf16 NT GEMM (radiance_gemm.py page, gemm_bf16_nt_m64):
  *   C[m,n] = bf16( sum_k x[m,k] * w[n,k] ), fp32 accumulation.
  * x: bf16 [M, K]; w: bf16 [N, K]; c: bf16 [M, N]; all contiguous row-major,
@@ -228,6 +244,14 @@ BS_API int gemm_bf16_skinny_noalloc(const void* x, const void* w, void* c, int M
 BS_API int add_rms_quant_fp8(const void* y, const void* residual, const void* gamma, float eps,
                              void* q, float* scale, void* residual_out, int M, int K,
                              bs_stream_t stream);
+
+/* The same producer writing the codes in the activation-tiled order that
+ * bsgemm_w4a8_mxfp4_atiled reads (see there); residual_out and scale as
+ * above.  q_tiled holds ceil(M/32)*32*K bytes, 16-byte aligned; the pad rows
+ * of the last 32-row block are not written.  K % 128 == 0, 128 <= K <= 32768. */
+BS_API int add_rms_quant_fp8_tiled(const void* y, const void* residual, const void* gamma, float eps,
+                                   void* q_tiled, float* scale, void* residual_out, int M, int K,
+                                   bs_stream_t stream);
 
 /* The same producer for the block-FP8 consumer: one scale per token per
  * 128-wide K group (the block-FP8 activation format of the radiance_kernels.py

@@ -40,6 +40,23 @@ def _w4_call(M, N, K, seed):
     return (lambda: bs.bsgemm_w4a8_mxfp4(a, s, desc, pre, out=out, ws=work)), [out]
 
 
+def _tiled_chain_call(M, N, K, seed):
+    """Tiled producer then tiled GEMM: two launches, one call each."""
+    wp, e = synth.mxfp4_weight_raw(12, seed, N, K)
+    pre, desc = bs.prelayout_mxfp4(dev_u8(wp), dev_u8(e))
+    y, r, g = (dev_bf16(v) for v in synth.producer_raw(seed, M, K))
+    q = torch.empty((bs.tiled_activation_bytes(M, K),), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M,), dtype=torch.float32, device="cuda")
+    ro = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    work = bs.alloc_workspace(bs.BS_OP_W4A8_MXFP4, M, N, K)
+
+    def fn():
+        bs.add_rms_quant_fp8_tiled(y, r, g, 1e-6, q, s, ro)
+        bs.bsgemm_w4a8_mxfp4_atiled(q, s, desc, pre, M, out=out, ws=work)
+    return fn, [s, ro, out]
+
+
 def _skinny_call(M, N, K, seed):
     xb, wb = synth.skinny_raw(seed, M, N, K)
     x, w = dev_bf16(xb), dev_bf16(wb)
@@ -93,6 +110,7 @@ def test_graph_replays_match_eager():
         _w4_call(8, 2048, 17408, 4),      # decode long-K configuration, split
         _w4_call(256, 1280, 5120, 5),     # small-tile prefill, K split
         _w4_call(4096, 5120, 1024, 6),    # large tiles + column strip
+        _tiled_chain_call(300, 1280, 1024, 8),   # activation-tiled producer + GEMM (split small tiles)
         _skinny_call(8, 256, 2048, 0),    # split over 4 workgroups
         _skinny_call(64, 96, 5120, 9),    # split over 10 workgroups
     ] + _producer_calls()
