@@ -379,7 +379,9 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
     // 12.7 -> 11.5 us, N = 34816 20.6 -> 17.7 us; slower at N = 5120 and
     // below 5 rows).
     const bool slice_halves_lds = static_cast<size_t>(d.rs) * 40 * 128 > kMaxDecodeLds / 2;
-    if (long_k) set(4, 2, 1, 8);
+    // long K: 12 waves of 8 steps (re-swept: M = 8 N = 5120 K = 17408
+    // 13.5 -> 12.4 us against TW=4 KW=2)
+    if (long_k) set(4, 3, 1, 8);
     else if (slice_halves_lds) set(1, 5, 2, 4);
     else if (M >= 5 && N / 16 >= 640) set(3, 5, 1, 8);
     else set(1, 10, 1, 4);
@@ -390,7 +392,10 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   } else if (mx) {
     set(8, 1, 1, 8);
   } else if (long_k) {
-    d.mb == 2 ? set(4, 2, 1, 8) : set(4, 2, 1, 4);
+    // 33..64 rows: 8 tiles x 8 steps per workgroup (re-swept once the scale
+    // loads stopped holding up the weight stream: M = 64 K = 17408 34.4 ->
+    // 32.2 us against TW=4 KW=2 R=4)
+    d.mb == 2 ? set(4, 2, 1, 8) : set(8, 1, 1, 8);
   } else if (wide_n) {
     set(8, 1, 1, 8);
   } else {
@@ -474,7 +479,7 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
   const int key = ((d.tw * 100 + d.kw) * 10 + d.t) * 100 + d.r;  // TW, KW, R < 100, T < 10
   if (mx) {
     if (d.mb == 1 && key == 110104) BS_DEC(true, 1, 1, 10, 1, 4);
-    else if (d.mb == 1 && key == 402108) BS_DEC(true, 1, 4, 2, 1, 8);
+    else if (d.mb == 1 && key == 403108) BS_DEC(true, 1, 4, 3, 1, 8);
     else if (d.mb == 1 && key == 105204) BS_DEC(true, 1, 1, 5, 2, 4);
     else if (d.mb == 1 && key == 305108) BS_DEC(true, 1, 3, 5, 1, 8);
     else if (d.mb == 2 && key == 801108) BS_DEC(true, 2, 8, 1, 1, 8);
@@ -488,7 +493,6 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     else if (d.mb == 2 && key == 402108) BS_DEC(false, 2, 4, 2, 1, 8);
     else if (d.mb == 2 && key == 801108) BS_DEC(false, 2, 8, 1, 1, 8);
     else if (d.mb == 4 && key == 404104) BS_DEC(false, 4, 4, 4, 1, 4);
-    else if (d.mb == 4 && key == 402104) BS_DEC(false, 4, 4, 2, 1, 4);
     else if (d.mb == 4 && key == 801108) BS_DEC(false, 4, 8, 1, 1, 8);
     else return BS_ERR_SHAPE;
   }
