@@ -275,8 +275,8 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
 
   // ---- 5. output: lane l holds C[m = l%16 (+16 mb)][n = 4(l/16) .. +3] -------
   auto store_bf16x4 = [&](int m, int n, v4f v) {
-    const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    const uint32_t lo = bf16x2_rne(v[0], v[1]);
+    const uint32_t hi = bf16x2_rne(v[2], v[3]);
     *reinterpret_cast<uint2*>(p.c + m * p.ldc + n) = uint2{lo, hi};
   };
   // (waves with kw > 0 stay to the end: they take part in every barrier)

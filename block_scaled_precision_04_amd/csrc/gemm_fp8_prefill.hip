@@ -219,8 +219,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
     for (int nb = 0; nb < kNB; ++nb) {
       const int piece = wn * (kBN / kWN / 4) + nb * 4 + q;
       const v4f v = acc[mb][nb];
-      const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      const uint32_t lo = bf16x2_rne(v[0], v[1]);
+      const uint32_t hi = bf16x2_rne(v[2], v[3]);
       *reinterpret_cast<uint2*>(lds + r * (kBN * 2) + (piece ^ ((r & 7) << 2)) * 8) = make_uint2(lo, hi);
     }
   }

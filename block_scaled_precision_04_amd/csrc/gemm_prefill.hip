@@ -372,22 +372,36 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int piece = (wn * (BN / WN) + 32 * p + 8 * i) / 4 + (l >> 5);
-          const uint32_t b0 = f32_to_bf16_rne(acc[p][q][4 * i + 0] * sc);
-          const uint32_t b1 = f32_to_bf16_rne(acc[p][q][4 * i + 1] * sc);
-          const uint32_t b2 = f32_to_bf16_rne(acc[p][q][4 * i + 2] * sc);
-          const uint32_t b3 = f32_to_bf16_rne(acc[p][q][4 * i + 3] * sc);
           *reinterpret_cast<uint2*>(lds + r * (BN * 2) + (piece ^ (r & 31)) * 8) =
-              make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+              make_uint2(bf16x2_rne(acc[p][q][4 * i + 0] * sc, acc[p][q][4 * i + 1] * sc),
+                         bf16x2_rne(acc[p][q][4 * i + 2] * sc, acc[p][q][4 * i + 3] * sc));
         }
       }
     }
     __syncthreads();
-    const int j = tid % kPieces, r0 = tid / kPieces;
-    const bool n_ok = n0 + 4 * j < N;  // N % 16 == 0: a piece is wholly inside or outside
+    if (ldc % 8 == 0) {
+      // 16-byte pieces: logical 8-byte pieces 2j and 2j+1 sit in the
+      // physical pair j ^ (s >> 1) (s = r % 32), swapped when s is odd
+      constexpr int kPairs = BN / 8;
+      constexpr int kRows2 = C::kThreads / kPairs;
+      static_assert(C::kThreads % kPairs == 0 && BM % kRows2 == 0, "wide store pass shape");
+      const int j = tid % kPairs, r0 = tid / kPairs;
+      const bool n_ok = n0 + 8 * j < N;  // N % 16 == 0: a 16-byte piece is wholly inside or outside
 #pragma unroll 4
-    for (int r = r0; r < BM; r += kRowsPerPass) {
-      const uint2 v = *reinterpret_cast<const uint2*>(lds + r * (BN * 2) + (j ^ (r & 31)) * 8);
-      if (n_ok && m0 + r < M) st_stream8(reinterpret_cast<uint2*>(c + (m0 + r) * ldc + n0 + 4 * j), v.x, v.y);
+      for (int r = r0; r < BM; r += kRows2) {
+        const int s = r & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + (j ^ (s >> 1)) * 16);
+        const uint4 o = (s & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+        if (n_ok && m0 + r < M) st_stream16(reinterpret_cast<uint4*>(c + (m0 + r) * ldc + n0 + 8 * j), o);
+      }
+    } else {
+      const int j = tid % kPieces, r0 = tid / kPieces;
+      const bool n_ok = n0 + 4 * j < N;  // N % 16 == 0: a piece is wholly inside or outside
+#pragma unroll 4
+      for (int r = r0; r < BM; r += kRowsPerPass) {
+        const uint2 v = *reinterpret_cast<const uint2*>(lds + r * (BN * 2) + (j ^ (r & 31)) * 8);
+        if (n_ok && m0 + r < M) st_stream8(reinterpret_cast<uint2*>(c + (m0 + r) * ldc + n0 + 4 * j), v.x, v.y);
+      }
     }
   };
   if (!SPLIT || S == 1) {

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     for (int v = 0; v < kWaves; ++v) s += red[v][mb * 4 + rr][lane];
     const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
     if (ksplit == 1) {
-      if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(s));
+      if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(bf16x2_rne(s, 0.0f));
     } else {
       __hip_atomic_store(&slab[(static_cast<size_t>(kb) * ntiles + nt) * (MB * 256) + o], s, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     const int o = threadIdx.x + 256 * i;
     const int lane = o & 63, rr = (o >> 6) & 3, mb = o >> 8;
     const int m = 16 * mb + (lane & 15), n = nt * 16 + 4 * (lane >> 4) + rr;
-    if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(tot[i]));
+    if (m < M) c[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(bf16x2_rne(tot[i], 0.0f));
   }
   if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

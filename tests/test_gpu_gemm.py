@@ -275,6 +275,25 @@ def test_skinny_guarded_out(M, N, K):
     checks.assert_gemm_close(host_bits16(out), ce, asum, f"skinny guarded M={M} N={N} K={K}")
 
 
+def test_w4a8_prefill_out_ldc_not_multiple_of_8():
+    """The prefill epilogue stores 16-byte pieces when the output's leading
+    dimension is a multiple of 8 elements and 8-byte pieces otherwise: here
+    ldc = N + 36 (4 mod 8), first row 16-byte aligned, a guard below and
+    beside the view."""
+    M, N, K = 150, 176, 640
+    aq, asc, wp, e = w4a8_inputs(8, 3, M, N, K)
+    big = torch.full((M + 1, N + 36), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[0:M, 8:8 + N]
+    assert view.stride(0) % 8 == 4
+    _w4_run(aq, asc, wp, e, out=view)
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[0:M, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 ldc 4 mod 8")
+
+
 def test_w4a8_large_tiles_strided_out():
     """The large-tile launch and its column strip writing into a strided view:
     M=4000 (last 256-row tile 160 rows deep), N=4240 -> 16 x 16 large tiles
