@@ -213,6 +213,114 @@ __global__ __launch_bounds__(T) void k_row_quant(const uint4* __restrict__ y,
   }
 }
 
+// The norm producer writing the activation-tiled order: four consecutive
+// rows per workgroup (T threads each, as k_row_quant), their codes gathered
+// in LDS, then written as whole 128-byte lines.  In the tiled order a row
+// owns 32-byte lane slots, never a whole line: four consecutive rows (4r ..
+// 4r+3, lanes 4r%32 .. +3 of one half step) fill one line, so a workgroup
+// holding them stores full lines instead of scattering 16-byte pieces
+// (measured: one row per workgroup took 43 us at M = 4096, K = 5120, against
+// 33 us for the row-major codes).  Per row the arithmetic is k_row_quant's
+// with NORM: residual add, fp64 sum of squares, h rounded once to fp32,
+// per-token scale, IEEE h / scale and the e4m3 convert.
+template <int NC, int T>
+__global__ __launch_bounds__(4 * T) void k_row_quant_tiled(const uint4* __restrict__ y, const uint4* res,
+                                                           const uint4* __restrict__ gamma, float eps,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                           uint4* rout, int M, int K) {
+  static_assert(T % 64 == 0, "whole waves");
+  constexpr int kW = T / 64;  // waves per row
+  __shared__ double red_d[4][kW];
+  __shared__ float red_f[4][kW];
+  extern __shared__ __align__(16) uint8_t codes[];  // [4][K] e4m3, row-major
+  const int rr = threadIdx.x / T;                    // row within the workgroup
+  const int t = threadIdx.x % T;
+  const int wv = t >> 6, l = t & 63;
+  const int row0 = blockIdx.x * 4;
+  const int row = min(row0 + rr, M - 1);            // rows past M redo row M-1 (never stored)
+  const int nch = K >> 3;
+  const size_t base = static_cast<size_t>(row) * nch;
+  uint4 yv[NC], rv[NC], gv[NC];
+  bool live[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = c * T + t;
+    live[c] = idx < nch;
+    const int ci = min(idx, nch - 1);
+    yv[c] = y[base + ci];
+    rv[c] = res[base + ci];
+    gv[c] = gamma[ci];
+  }
+  float h[NC][8];
+  double ss = 0.0;
+  const bool own = row0 + rr < M;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float a[8], b[8];
+    unpack8(yv[c], a);
+    unpack8(rv[c], b);
+    uint32_t rb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rb[j] = f32_to_bf16_rne(a[j] + b[j]);
+      h[c][j] = live[c] ? __uint_as_float(rb[j] << 16) : 0.0f;
+      ss += static_cast<double>(h[c][j]) * static_cast<double>(h[c][j]);
+    }
+    if (live[c] && own)
+      st_stream16(rout + base + c * T + t, make_uint4(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16),
+                                                      rb[4] | (rb[5] << 16), rb[6] | (rb[7] << 16)));
+  }
+  // per-row reductions: the row's kW waves through LDS slots of their own
+  ss = wave_sum_f64(ss);
+  if (l == 0) red_d[rr][wv] = ss;
+  __syncthreads();
+  double tot = red_d[rr][0];
+#pragma unroll
+  for (int i = 1; i < kW; ++i) tot += red_d[rr][i];
+  const double inv = 1.0 / sqrt(tot / static_cast<double>(K) + static_cast<double>(eps));
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float g[8];
+    unpack8(gv[c], g);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[c][j] = static_cast<float>(static_cast<double>(h[c][j]) * inv * (1.0 + static_cast<double>(g[j])));
+      amax = fmaxf(amax, fabsf(h[c][j]));
+    }
+  }
+  amax = wave_max(amax);
+  if (l == 0) red_f[rr][wv] = amax;
+  __syncthreads();
+  amax = red_f[rr][0];
+#pragma unroll
+  for (int i = 1; i < kW; ++i) amax = fmaxf(amax, red_f[rr][i]);
+  const float s = fmaxf(amax / kFp8Max, static_cast<float>(kMinScale));
+  if (t == 0 && own) scale[row] = s;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = c * T + t;
+    if (idx < nch) *reinterpret_cast<uint2*>(codes + rr * K + idx * 8) = quant8(h[c], s);
+  }
+  __syncthreads();
+  // whole lines: line (ks, h, g) of this row quad is 4 rows x 32 bytes; its
+  // 16-byte unit u holds row u/2, bytes 16c .. +15 (c = u%2) of the row's
+  // lane slot = K offsets 128ks + 64h + 32c + 16g .. +15
+  const int rows = min(4, M - row0);
+  const int KS = K >> 7;
+  const int lines = KS * 4;
+  uint8_t* qb = q + ((static_cast<size_t>(row0 >> 5) * KS) * 2) * 2048 + (row0 & 31) * 32;
+  for (int v = threadIdx.x; v < lines * 8; v += 4 * T) {
+    const int line = v >> 3, u = v & 7;
+    const int r = u >> 1, c = u & 1;
+    const int ks = line >> 2, hh = (line >> 1) & 1, g = line & 1;
+    if (r < rows) {
+      const uint4 val = *reinterpret_cast<const uint4*>(codes + r * K + ks * 128 + hh * 64 + 32 * c + 16 * g);
+      st_stream16(reinterpret_cast<uint4*>(qb + ((static_cast<size_t>(ks) * 2 + hh) * 2048) + g * 1024 + u * 16), val);
+    }
+  }
+}
+
 // One scale per 128-wide group of each row.  Block = 256 threads = 16 groups
 // of 16 threads, each thread one 8-element chunk.  grid = (ceil(K/2048), M).
 __global__ __launch_bounds__(kThreads) void k_group_quant(const uint4* __restrict__ x, uint2* __restrict__ q,
@@ -421,8 +529,33 @@ BS_API int add_rms_quant_fp8_tiled(const void* y, const void* residual, const vo
                bs_aligned(scale, 4) && bs_aligned(residual_out, 16),
            BS_ERR_ALIGN);
   BS_CHECK(eps >= 0.0f, BS_ERR_ARG);
-  return launch_row_quant<true, false, true>(y, residual, gamma, eps, q_tiled, scale, residual_out, M, K,
-                                             static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t lds = static_cast<size_t>(4) * K;   // the row quad's codes
+  const dim3 grid((M + 3) / 4);
+#define BS_ROWQT(N_, T_)                                                                                     \
+  do {                                                                                                       \
+    auto* fn = &k_row_quant_tiled<N_, T_>;                                                                   \
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                    \
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 5120);       \
+    if (attr != hipSuccess) return BS_ERR_LAUNCH;                                                            \
+    fn<<<grid, dim3(4 * T_), lds, st>>>(static_cast<const uint4*>(y), static_cast<const uint4*>(residual),   \
+                                        static_cast<const uint4*>(gamma), eps, static_cast<uint8_t*>(q_tiled), \
+                                        scale, static_cast<uint4*>(residual_out), M, K);                     \
+  } while (0)
+  // row quads of 128-thread rows, up to five chunks per thread (K <= 5120:
+  // 512 threads per workgroup, two waves per SIMD); longer rows would need
+  // more registers than four rows per workgroup leave, and keep one row per
+  // workgroup with scattered 8-byte stores
+  const int nc128 = (K / 8 + 127) / 128;
+  if (nc128 > 5)
+    return launch_row_quant<true, false, true>(y, residual, gamma, eps, q_tiled, scale, residual_out, M, K, st);
+  if (nc128 <= 1) BS_ROWQT(1, 128);
+  else if (nc128 <= 2) BS_ROWQT(2, 128);
+  else if (nc128 <= 3) BS_ROWQT(3, 128);
+  else if (nc128 <= 4) BS_ROWQT(4, 128);
+  else BS_ROWQT(5, 128);
+#undef BS_ROWQT
+  return bs_launch_status();
 }
 
 BS_API int add_rms_quant_fp8_group128(const void* y, const void* residual, const void* gamma, float eps, void* q,

@@ -24,7 +24,7 @@ from tests.gpu_util import (dev_u8, dev_bf16, dev_f32, host_bits16, w4a8_inputs,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,K", [(65, 128), (100, 384), (333, 5120), (4096, 5120)])
+@pytest.mark.parametrize("M,K", [(65, 128), (100, 384), (333, 5120), (4096, 5120), (70, 8192), (37, 1024)])
 def test_tiled_producer_matches_row_major_and_oracle(M, K):
     y, r, w = synth.producer_raw(M % 7, M, K)
     q, s, ro = bs.add_rms_quant_fp8(dev_bf16(y), dev_bf16(r), dev_bf16(w), 1e-6)
