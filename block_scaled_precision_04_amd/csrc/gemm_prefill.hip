@@ -36,12 +36,16 @@
 // at any moment share a few activation and weight tiles in that XCD's L2.
 #include <algorithm>
 #include <numeric>
+#include <type_traits>
 
 #include "common.h"
 
 namespace {
 
 BS_INLINE int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+constexpr std::true_type kWithDma{};
+constexpr std::false_type kNoDma{};
 
 template <int BM, int BN, int WM, int WN>
 struct PrefillCfg {
@@ -56,10 +60,13 @@ struct PrefillCfg {
   static constexpr int kAIters = kAStage / (kThreads * 16);
   static constexpr int kBIters = kBStage / (kThreads * 16);
   static constexpr int kSIters = (kSStage + kThreads * 16 - 1) / (kThreads * 16);
-  // direct-to-LDS loads per stage issued by every wave (waves past the scale
-  // region skip its load, so this is the count the slowest-issuing wave has)
-  static constexpr int kDmaMin = kAIters + kBIters + kSStage / (kThreads * 16);
-  static constexpr int kDmaAll = kAIters + kBIters + kSIters;
+  static constexpr int kSPieces = kSStage / 1024;  // one wave-wide 16-byte load each
+  // direct-to-LDS loads per stage, the same for every wave: where the e8m0
+  // region has fewer 1 KiB pieces than the waves' loads cover, the waves past
+  // it repeat an earlier wave's piece (same source, same LDS bytes, identical
+  // values), so no load is conditional on the wave and the K loop has no
+  // branch for the scheduler to stop at
+  static constexpr int kDma = kAIters + kBIters + kSIters;
   static_assert(kAStage % (kThreads * 16) == 0 && kBStage % (kThreads * 16) == 0, "tile / thread mismatch");
   static_assert(kSStage % 1024 == 0, "scale stage must be whole waves");
   static_assert(kTM >= 1 && kTN >= 1, "wave tile too small");
@@ -130,11 +137,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   uint32_t soff_g[C::kSIters];
 #pragma unroll
   for (int i = 0; i < C::kSIters; ++i) {
-    const int p = (i * C::kWaves + wave) * 64 + l;
+    const int p = ((i * C::kWaves + wave) % C::kSPieces) * 64 + l;
     const int nt = min(nt0 + (p >> 4), NT - 1);
     soff_g[i] = static_cast<uint32_t>(nt) * static_cast<uint32_t>(KQ) * 256u + static_cast<uint32_t>((p & 15) * 16);
   }
-  // the i-th direct-to-LDS load of step ks (i < kDmaAll) into buffer buf
+  // the i-th direct-to-LDS load of step ks (i < kDma) into buffer buf
   auto dma_one = [&](int i, int ks, int buf) {
     const uint32_t base = lds0 + buf * C::kStage;
     if (i < C::kAIters) {
@@ -144,8 +151,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       dma16(base + C::kAStage + (j * C::kWaves + wave) * 1024, w + static_cast<size_t>(ks) * 1024, boff_g[j]);
     } else {
       const int j = i - C::kAIters - C::kBIters;
-      if (C::kSStage % (C::kThreads * 16) == 0 || (j * C::kWaves + wave) * 1024 < C::kSStage)
-        dma16(base + C::kAStage + C::kBStage + (j * C::kWaves + wave) * 1024, wsc + (ks >> 2) * 256, soff_g[j]);
+      dma16(base + C::kAStage + C::kBStage + ((j * C::kWaves + wave) % C::kSPieces) * 1024, wsc + (ks >> 2) * 256,
+            soff_g[j]);
     }
   };
 
@@ -204,10 +211,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll
     for (int q = 0; q < C::kTM; ++q) f.a[q] = a_frag(st, hh, q);
   };
-  // MFMAs of one half step; with dks >= 0 the loads of step dks (into buffer
+  // MFMAs of one half step; with DMA the loads of step dks (into buffer
   // dbuf) are issued between them (one after each MFMA), so the load unit is
   // fed steadily and the wave never stalls on a burst of loads
-  auto mma = [&](const Frag& f, int sh, int dks, int dbuf) {
+  // (DMA is a compile-time flag, so that the K loop holds no branch on it)
+  auto mma = [&](const Frag& f, int sh, auto dma, int dks, int dbuf) {
+    constexpr bool DMA = decltype(dma)::value;
 #pragma unroll
     for (int p = 0; p < C::kTN; ++p) {
       const int sc = static_cast<int>(f.s[p] >> sh);
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       for (int q = 0; q < C::kTM; ++q) {
         acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[p], f.a[q], acc[p][q], 4, 0, 0, sc, 0, 127);
         const int i = p * C::kTM + q;
-        if (i < C::kDmaAll && dks >= 0) {
+        if (DMA && i < C::kDma) {
           __builtin_amdgcn_sched_barrier(0);
           dma_one(i, dks, dbuf);
           __builtin_amdgcn_sched_barrier(0);
@@ -224,8 +233,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     }
     // loads left over when a half step has fewer MFMAs than loads
 #pragma unroll
-    for (int i = C::kTN * C::kTM; i < C::kDmaAll; ++i)
-      if (dks >= 0) dma_one(i, dks, dbuf);
+    for (int i = C::kTN * C::kTM; i < C::kDma; ++i)
+      if (DMA) dma_one(i, dks, dbuf);
   };
 
   // one LDS read "piece" of a fragment set: pieces 0..kTN-1 are the weight
@@ -251,33 +260,38 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
         acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[p], f.a[q], acc[p][q], 4, 0, 0, sc, 0, 127);
         const int i = p * C::kTM + q;
         __builtin_amdgcn_sched_barrier(0);
-        if (i < C::kDmaAll && dks >= 0) dma_one(i, dks, dbuf);
+        if (i < C::kDma && dks >= 0) dma_one(i, dks, dbuf);
         if (i < C::kTN + C::kTM) lds_piece(rst, rhh, rf, i);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int i = C::kTN * C::kTM; i < C::kDmaAll; ++i)
+    for (int i = C::kTN * C::kTM; i < C::kDma; ++i)
       if (dks >= 0) dma_one(i, dks, dbuf);
 #pragma unroll
     for (int i = C::kTN * C::kTM; i < C::kTN + C::kTM; ++i) lds_piece(rst, rhh, rf, i);
   };
-  // Pipeline (the plain schedule, used with the 128x128 tile): three LDS buffers (buffer of step s = s % 3) and three fragment
-  // register sets rotating over the 64-K halves.  The matrix unit queues a
-  // wave's MFMAs and reads their operand registers only when each one starts,
-  // so a register set is refilled only once the MFMAs that read it are two
-  // halves back in the queue.  Step s, with sets (X, Y, Z):
+  // Pipeline (the plain schedule, used with the 128x128 tile): three LDS
+  // buffers (buffer of step s = s % 3) and three fragment register sets
+  // rotating over the 64-K halves.  The matrix unit queues a wave's MFMAs and
+  // reads their operand registers only when each one starts, so a register
+  // set is refilled only once the MFMAs that read it are two halves back in
+  // the queue.  Step s, with sets (X, Y, Z):
   //   MFMAs on X (first half of s), with the loads of step s+2 (into the
   //   buffer step s-1 used) issued one per MFMA; refill Y with the second half
   //   of s; MFMAs on Y; wait until this wave's loads of step s+1 have landed
   //   and its LDS reads are done; barrier (publishes step s+1, frees buffer s
   //   for step s+3); refill Z with the first half of step s+1.
   // The next step uses (Z, X, Y).  The loads stay two steps ahead of their use.
+  // (A variant with the barrier in mid-step, the loads three steps ahead and
+  // the next step's first fragments read under the second half's MFMAs ran
+  // no faster: with two workgroups per CU the other wave on each SIMD covers
+  // the LDS reads after the barrier.)
 #pragma unroll
-  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, k_begin, 0);
+  for (int i = 0; i < C::kDma; ++i) dma_one(i, k_begin, 0);
 #pragma unroll
-  for (int i = 0; i < C::kDmaAll; ++i) dma_one(i, min(k_begin + 1, k_end - 1), 1);
-  wait_vm<C::kDmaMin>();
+  for (int i = 0; i < C::kDma; ++i) dma_one(i, min(k_begin + 1, k_end - 1), 1);
+  wait_vm<C::kDma>();
   __syncthreads();
   Frag f0, f1, f2;
   lds_frags(lds, 0, f0);
@@ -289,13 +303,13 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     int pbuf = buf + 2;
     if (pbuf >= STAGES) pbuf -= STAGES;
     __builtin_amdgcn_sched_barrier(0);
-    mma(fx, sh, min(ks + 2, k_end - 1), pbuf);
+    mma(fx, sh, kWithDma, min(ks + 2, k_end - 1), pbuf);
     __builtin_amdgcn_sched_barrier(0);
     lds_frags(st, 1, fy);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fy, sh, -1, 0);
+    mma(fy, sh, kNoDma, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<C::kDmaMin>();
+    wait_vm<C::kDma>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
     buf = buf + 1 == STAGES ? 0 : buf + 1;

@@ -26,6 +26,14 @@ cross-compiles without a GPU; each source is compiled once per session).
   may still be outstanding.  If the compiler sinks a scale load below the
   weight loads, the wait before the LDS store of the scales covers the whole
   weight stream and the kernel serialises load and compute.
+* Prefill K loop shape: the MXFP4 prefill kernels issue each half step's
+  MFMAs with the next stages' direct-to-LDS loads between them.  MFMAs have
+  no memory effects, so the compiler may move them across the loop's
+  barriers and branches; a wave-dependent branch in the loop (e.g. a load
+  that only some waves issue) once let it gather the MFMAs of three K steps
+  into one run after the last barrier, which serialised loads and compute
+  and cost 10-17% on the 128x128 tile.  No run of back-to-back MFMAs may be
+  longer than one half step's, and the loads must sit between MFMAs.
 """
 import functools
 import glob
@@ -138,3 +146,29 @@ def test_scaled_16x16x128_mfma_accumulates_in_vgprs(src):
             if s.startswith("v_mfma_scale_f32_16x16x128_f8f6f4"):
                 dst = s.split()[1]
                 assert dst.startswith("v["), f"{name}: scaled 16x16x128 MFMA writes {dst}: {s}"
+
+
+def test_prefill_k_loop_keeps_mfmas_and_loads_interleaved():
+    seen = 0
+    for name, ins in _kernels(_asm("gemm_prefill.hip")):
+        m = re.search(r"k_w4a8_prefillILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name)
+        if not m:
+            continue
+        bm, bn, wm, wn = (int(x) for x in m.groups())
+        half = (bm // wm // 32) * (bn // wn // 32)   # MFMAs per wave per 64-K half step
+        dma = (bm * 128 + bn * 64) // (64 * wm * wn * 16) + -(-(bn * 16) // (64 * wm * wn * 16))
+        run = longest = interleaved = 0
+        for i, s in enumerate(ins):
+            if s.startswith("v_mfma"):
+                run += 1
+                longest = max(longest, run)
+                nxt = next((j for j in range(i + 1, len(ins)) if ins[j].startswith("v_mfma")), len(ins))
+                if any(x.startswith("global_load_lds") for x in ins[i + 1:nxt]):
+                    interleaved += 1
+            elif not s.startswith(("s_waitcnt", "s_nop")):
+                run = 0
+        assert longest <= half, f"{name}: {longest} back-to-back MFMAs, one half step has {half}"
+        # the three unrolled steps of the loop each put min(half, loads) loads right after MFMAs
+        assert interleaved >= 3 * min(half, dma), f"{name}: only {interleaved} MFMAs followed by a load"
+        seen += 1
+    assert seen == 4, f"{seen} prefill instantiations found"
