@@ -58,7 +58,10 @@ static_assert(kSWaves < kWaves, "one more wave loads the weight scales");
 static_assert(kAStage % (kThreads * 16) == 0 && kBStage % (kThreads * 16) == 0, "stage / thread mismatch");
 static_assert(kBN / kWN == 128, "a wave's columns must fill one weight-scale block");
 
-BS_INLINE int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// 16-byte chunk c of activation row r sits at slot c ^ ((r / 2) % 8): a
+// fragment read (one chunk of 16 consecutive rows) then covers the 16 slots of
+// a 256-byte LDS line once, which gfx950's 64 banks serve in one pass
+BS_INLINE int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 BS_INLINE v8i pack8(uint4 x, uint4 y) {
   return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }

@@ -19,9 +19,13 @@
 // as pre-laid-out) are moved global -> LDS by the direct-to-LDS 16-byte load
 // (no register staging) into one of three stage buffers: the loads of step
 // k+2 are issued while step k is computed.  Activation rows are stored
-// without padding; their eight 16-byte chunks are XOR-swizzled by the row
-// index so that the fragment reads (32 rows, same chunk) spread over the LDS
-// banks.  The per-token activation scale multiplies the accumulator in the
+// without padding; their eight 16-byte chunks are XOR-swizzled by bits 1..3
+// of the row index.  gfx950's LDS has 64 four-byte banks and serves a 16-byte
+// read 16 lanes at a time, so a read is conflict-free when its 16 lanes hit
+// 16 distinct 16-byte slots of a 256-byte line; the fragment reads take one
+// chunk of 16 consecutive rows, two rows per 256 bytes, and the swizzle by
+// (row / 2) % 8 gives each row pair the eight slots (measured: the swizzle by
+// row % 8 served these reads in two passes).  The per-token activation scale multiplies the accumulator in the
 // epilogue, then bf16 RNE and store.  The first MFMA operand is the weight
 // (rows = n), the second the activation (rows = m), so each lane holds four
 // consecutive n of one m; the epilogue regroups them in LDS into whole output
@@ -42,7 +46,7 @@
 
 namespace {
 
-BS_INLINE int swz(int row, int chunk) { return chunk ^ (row & 7); }
+BS_INLINE int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 constexpr std::true_type kWithDma{};
 constexpr std::false_type kNoDma{};
