@@ -39,6 +39,14 @@ def build(verbose=False):
         seen = sorted({l.split("warning:", 1)[1].strip() for l in out.splitlines() if "warning:" in l})
         for w in seen:
             print(f"libbsgemm build warning: {w}")
+    # every symbol must resolve: a kernel whose host-side launch stub the
+    # compiler dropped (e.g. after a device-only construct in code it also
+    # compiles for the host) links without error and fails only when loaded
+    undef = subprocess.run(["nm", "-D", "--undefined-only", "-C", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in undef.stdout.splitlines() if "device_stub" in l or "anonymous namespace" in l]
+    if undef.returncode == 0 and missing:
+        os.remove(tmp)
+        raise RuntimeError("libbsgemm build left symbols unresolved:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -107,6 +107,12 @@ BS_INLINE void dma4(uint32_t lds_addr, const void* sbase, uint32_t voff) {
                : "memory", "m0");
 }
 
+// An empty statement that takes x in VGPRs: x stays live, in the registers it
+// already has, up to this point of the program.
+BS_INLINE void keep_vgprs(v4i x) { asm volatile("" ::"v"(x)); }
+BS_INLINE void keep_vgprs(v8i x) { asm volatile("" ::"v"(x)); }
+BS_INLINE void keep_vgprs(uint32_t x) { asm volatile("" ::"v"(x)); }
+
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads outstanding
 template <int N>
 BS_INLINE void wait_vm() {

@@ -276,49 +276,89 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     for (int i = C::kTN * C::kTM; i < C::kTN + C::kTM; ++i) lds_piece(rst, rhh, rf, i);
   };
   // Pipeline (the plain schedule, used with the 128x128 tile): three LDS
-  // buffers (buffer of step s = s % 3) and three fragment register sets
-  // rotating over the 64-K halves.  The matrix unit queues a wave's MFMAs and
-  // reads their operand registers only when each one starts, so a register
-  // set is refilled only once the MFMAs that read it are two halves back in
-  // the queue.  Step s, with sets (X, Y, Z):
-  //   MFMAs on X (first half of s), with the loads of step s+2 (into the
-  //   buffer step s-1 used) issued one per MFMA; refill Y with the second half
-  //   of s; MFMAs on Y; wait until this wave's loads of step s+1 have landed
-  //   and its LDS reads are done; barrier (publishes step s+1, frees buffer s
-  //   for step s+3); refill Z with the first half of step s+1.
-  // The next step uses (Z, X, Y).  The loads stay two steps ahead of their use.
-  // (A variant with the barrier in mid-step, the loads three steps ahead and
-  // the next step's first fragments read under the second half's MFMAs ran
-  // no faster: with two workgroups per CU the other wave on each SIMD covers
-  // the LDS reads after the barrier.)
+  // buffers (buffer of step s = s % 3) and fragment register sets rotating
+  // over the 64-K halves.  A half step has only four MFMAs per wave (128 ns),
+  // about the latency of its fragment reads, so every read is issued under
+  // the MFMAs of the half before it.  Step s, with sets (X, Y, Z):
+  //   MFMAs on X (first half of s), the LDS reads of Y (second half of s)
+  //   issued after the first of them; wait until this wave's loads of step s+1
+  //   have landed and its reads are done; barrier in mid-step (step s+1
+  //   published; every wave is done with buffer s); MFMAs on Y, with the
+  //   loads of step s+3 into buffer s and the reads of Z (first half of
+  //   s+1) issued between them.
+  // The next step uses (Z, X, Y).  The loads of a step are issued a step and
+  // a half before the barrier that publishes it.
+  auto mma_rd = [&](const Frag& f, int sh, auto dma, int dks, int dbuf, const uint8_t* rst, int rhh, Frag& rf) {
+    constexpr bool DMA = decltype(dma)::value;
+#pragma unroll
+    for (int p = 0; p < C::kTN; ++p) {
+      const int sc = static_cast<int>(f.s[p] >> sh);
+#pragma unroll
+      for (int q = 0; q < C::kTM; ++q) {
+        acc[p][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[p], f.a[q], acc[p][q], 4, 0, 0, sc, 0, 127);
+        const int i = p * C::kTM + q;
+        __builtin_amdgcn_sched_barrier(0);
+        if (DMA && i < C::kDma) dma_one(i, dks, dbuf);
+        if (i == 0) {
+          // every read of the next set, in the order its MFMAs use them:
+          // weight 0, the activations, then the other weights
+          lds_piece(rst, rhh, rf, 0);
+#pragma unroll
+          for (int j = 0; j < C::kTM; ++j) lds_piece(rst, rhh, rf, C::kTN + j);
+#pragma unroll
+          for (int j = 1; j < C::kTN; ++j) lds_piece(rst, rhh, rf, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int i = C::kTN * C::kTM; i < C::kDma; ++i)
+      if (DMA) dma_one(i, dks, dbuf);
+  };
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) dma_one(i, k_begin, 0);
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) dma_one(i, min(k_begin + 1, k_end - 1), 1);
-  wait_vm<C::kDma>();
+  if constexpr (!IL) {
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i) dma_one(i, min(k_begin + 2, k_end - 1), 2);
+    wait_vm<2 * C::kDma>();
+  } else {
+    wait_vm<C::kDma>();
+  }
   __syncthreads();
   Frag f0, f1, f2;
   lds_frags(lds, 0, f0);
 
   int buf = 0;
+  // A set whose MFMAs were just issued is dead to the register allocator,
+  // which then hands its registers to the next refill: the LDS reads would
+  // overwrite operands of MFMAs still in the queue.  keep() marks a set live
+  // up to the point where it stands, so each refill gets registers of its own.
+  auto keep = [&](const Frag& f) {
+#pragma unroll
+    for (int p = 0; p < C::kTN; ++p) {
+      keep_vgprs(__builtin_shufflevector(f.b[p], f.b[p], 0, 1, 2, 3));
+      keep_vgprs(f.s[p]);
+    }
+#pragma unroll
+    for (int q = 0; q < C::kTM; ++q) keep_vgprs(f.a[q]);
+  };
   auto step = [&](int ks, Frag& fx, Frag& fy, Frag& fz) {
-    const uint8_t* st = lds + buf * C::kStage;
     const int sh = 8 * (ks & 3);
-    int pbuf = buf + 2;
-    if (pbuf >= STAGES) pbuf -= STAGES;
+    const int nbuf = buf + 1 == STAGES ? 0 : buf + 1;
     __builtin_amdgcn_sched_barrier(0);
-    mma(fx, sh, kWithDma, min(ks + 2, k_end - 1), pbuf);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_frags(st, 1, fy);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(fy, sh, kNoDma, 0, 0);
+    mma_rd(fx, sh, kNoDma, 0, 0, lds + buf * C::kStage, 1, fy);
+    keep(fx);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<C::kDma>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    buf = buf + 1 == STAGES ? 0 : buf + 1;
+    __builtin_amdgcn_sched_barrier(0);
     // (after the last step this reads a buffer whose values are never used)
-    lds_frags(lds + buf * C::kStage, 0, fz);
+    mma_rd(fy, sh, kWithDma, min(ks + 3, k_end - 1), buf, lds + nbuf * C::kStage, 0, fz);
+    keep(fy);
+    buf = nbuf;
   };
   // The interleaved schedule (IL, used with the 256x256 tile), step s: this
   // wave's loads of step s+1 landed and its LDS reads done ->
