@@ -46,6 +46,7 @@ BS_API const char* bs_status_string(int status) {
     case BS_ERR_WORKSPACE: return "workspace missing or too small";
     case BS_ERR_LAUNCH: return "kernel launch failed";
     case BS_ERR_ARG: return "invalid argument";
+    case BS_ERR_DEVICE: return "no usable device, or the stream belongs to another device";
     case BS_ERR_SCRATCH: return "shape needs more than the static scratch array";
     default: return "unknown status";
   }
@@ -53,9 +54,29 @@ BS_API const char* bs_status_string(int status) {
 
 BS_API int bs_version(void) { return 100; }
 
+namespace {
+// A weight descriptor is accepted only when every field is what the
+// pre-layout of this shape writes (bs_prelayout_fp8_block /
+// bs_prelayout_mxfp4): one filled by hand, or for another shape or layout,
+// is refused with BS_ERR_LAYOUT before anything is read through it.
+bool fp8_desc_ok(const bs_wdesc* d, int N, int K) {
+  const uint64_t codes = static_cast<uint64_t>(N) * static_cast<uint64_t>(K);
+  return d->magic == BS_WDESC_MAGIC && d->layout == BS_LAYOUT_FP8_BLOCK && d->N == N && d->K == K &&
+         d->codes_bytes == codes && d->scales_offset == 0 && d->scales_bytes == 0 && d->total_bytes == codes;
+}
+bool mx_desc_ok(const bs_wdesc* d, int N, int K) {
+  const uint64_t codes = static_cast<uint64_t>(N) * static_cast<uint64_t>(K) / 2;
+  const uint64_t off = (codes + 255) / 256 * 256;
+  const uint64_t scales = static_cast<uint64_t>(N / 16) * static_cast<uint64_t>((K / 128 + 3) / 4) * 256;
+  return d->magic == BS_WDESC_MAGIC && d->layout == BS_LAYOUT_MXFP4 && d->N == N && d->K == K &&
+         d->codes_bytes == codes && d->scales_offset == off && d->scales_bytes == scales &&
+         d->total_bytes == off + scales;
+}
+}  // namespace
+
 BS_API size_t bs_workspace_bytes(int op, int M, int N, int K) {
   if (op == BS_OP_BF16_SKINNY) {
-    if (M < 1 || M > kSkinnyMaxM || N < 16 || N % 16 || K < 128 || K % 128) return 0;
+    if (M < 1 || M > kSkinnyMaxM || N < 16 || N % 16 || K < 32 || K % 32) return 0;
     return bs_skinny_workspace(M, N, K);
   }
   if (op == BS_OP_FP8_BLOCK) {
@@ -76,8 +97,7 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
   if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(a && a_scale && wd && w_pre && w_scale && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= kFp8MaxM && N >= 128 && N % 128 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
-  BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_FP8_BLOCK && wd->N == N && wd->K == K,
-           BS_ERR_LAYOUT);
+  BS_CHECK(fp8_desc_ok(wd, N, K), BS_ERR_LAYOUT);
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(lda < (1 << 25), BS_ERR_SHAPE);  // activation rows are addressed with 32-bit offsets
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 16) && bs_aligned(c, 16) && bs_aligned(a_scale, 4) &&
@@ -108,9 +128,7 @@ BS_API int bsgemm_w4a8_mxfp4(const void* a, int64_t lda, const float* a_scale, c
   if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(a && a_scale && wd && w_pre && c, BS_ERR_NULL);
   BS_CHECK(M >= 1 && M <= (1 << 22) && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
-  BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_MXFP4 && wd->N == N && wd->K == K &&
-               wd->scales_offset % 256 == 0 && wd->scales_offset >= wd->codes_bytes,
-           BS_ERR_LAYOUT);
+  BS_CHECK(mx_desc_ok(wd, N, K), BS_ERR_LAYOUT);
   BS_CHECK(lda >= K && lda % 16 == 0 && ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(bs_aligned(a, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
            BS_ERR_ALIGN);
@@ -140,9 +158,7 @@ BS_API int bsgemm_w4a8_mxfp4_atiled(const void* a_tiled, const float* a_scale, c
   BS_CHECK(a_tiled && a_scale && wd && w_pre && c, BS_ERR_NULL);
   BS_CHECK(M > kW4A8DecodeMaxM && M <= (1 << 22) && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0,
            BS_ERR_SHAPE);
-  BS_CHECK(wd->magic == BS_WDESC_MAGIC && wd->layout == BS_LAYOUT_MXFP4 && wd->N == N && wd->K == K &&
-               wd->scales_offset % 256 == 0 && wd->scales_offset >= wd->codes_bytes,
-           BS_ERR_LAYOUT);
+  BS_CHECK(mx_desc_ok(wd, N, K), BS_ERR_LAYOUT);
   BS_CHECK(ldc >= N && ldc % 4 == 0, BS_ERR_ALIGN);
   BS_CHECK(bs_aligned(a_tiled, 16) && bs_aligned(w_pre, 256) && bs_aligned(c, 16) && bs_aligned(a_scale, 4),
            BS_ERR_ALIGN);
@@ -162,7 +178,7 @@ BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N,
                             bs_stream_t stream) {
   if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(x && w && c, BS_ERR_NULL);
-  BS_CHECK(M >= 1 && M <= kSkinnyMaxM && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
+  BS_CHECK(M >= 1 && M <= kSkinnyMaxM && N >= 16 && N % 16 == 0 && K >= 32 && K % 32 == 0, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(w, 16) && bs_aligned(c, 4), BS_ERR_ALIGN);
   const int wst = check_workspace(bs_skinny_workspace(M, N, K), ws, ws_bytes);
   if (wst != BS_OK) return wst;

@@ -46,15 +46,23 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0, 0, 0, 0};
   if (chunk * kChunk < K) {
+    // K % 32 == 0: a lane's 32 K values are wholly inside or past K.  A lane
+    // past K (in a last, partial chunk) re-reads the row's last 32 values
+    // and zeroes its weight, so it adds nothing.
     const int k0 = chunk * kChunk + 32 * (l >> 4);
-    const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(nt * 16 + (l & 15)) * K + k0);
+    const bool k_in = k0 < K;
+    const int kl = k_in ? k0 : K - 32;
+    const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(nt * 16 + (l & 15)) * K + kl);
     uint4 wv[4], xv[MB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wv[j] = wr[j];
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = wr[j];
+      wv[j] = k_in ? v : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = min(16 * mb + (l & 15), M - 1);
-      const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + k0);
+      const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + kl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) xv[mb][j] = xr[j];
     }
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
 
 }  // namespace
 
-int bs_skinny_ksplit(int K) { return (K / kChunk + kWaves - 1) / kWaves; }
+int bs_skinny_ksplit(int K) { return ((K + kChunk - 1) / kChunk + kWaves - 1) / kWaves; }
 
 namespace {
 int skinny_mb(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
@@ -169,10 +177,10 @@ __global__ void k_zero_words(int* __restrict__ p, int n) {
 // that the clear is also valid if it lands inside a captured graph).
 int scratch_for(hipStream_t st, void** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BS_ERR_ARG;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BS_ERR_DEVICE;
   if (st != nullptr) {
     int sdev = -1;
-    if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return BS_ERR_ARG;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return BS_ERR_DEVICE;
   }
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_ptr[dev] == nullptr) {
@@ -192,7 +200,7 @@ extern "C" BS_API int gemm_bf16_skinny_noalloc(const void* x, const void* w, voi
                                                bs_stream_t stream) {
   if (M == 0) return BS_OK;  // an empty batch: nothing is read or launched
   BS_CHECK(x && w && c, BS_ERR_NULL);
-  BS_CHECK(M >= 1 && M <= 64 && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0, BS_ERR_SHAPE);
+  BS_CHECK(M >= 1 && M <= 64 && N >= 16 && N % 16 == 0 && K >= 32 && K % 32 == 0, BS_ERR_SHAPE);
   BS_CHECK(bs_aligned(x, 16) && bs_aligned(w, 16) && bs_aligned(c, 4), BS_ERR_ALIGN);
   const size_t need = bs_skinny_workspace(M, N, K);
   BS_CHECK(need <= kScratchBytes, BS_ERR_SCRATCH);

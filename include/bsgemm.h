@@ -55,8 +55,10 @@ enum {
   BS_ERR_LAYOUT = -4,    /* weight descriptor does not match the call          */
   BS_ERR_WORKSPACE = -5, /* workspace missing or smaller than required         */
   BS_ERR_LAUNCH = -6,    /* the HIP runtime refused a launch                   */
-  BS_ERR_ARG = -7,       /* any other invalid argument                         */
-  BS_ERR_SCRATCH = -8    /* the shape needs more than the static scratch array */
+  BS_ERR_DEVICE = -7,    /* no usable current device, or the stream is on      */
+                         /* another device                                     */
+  BS_ERR_SCRATCH = -8,   /* the shape needs more than the static scratch array */
+  BS_ERR_ARG = -9        /* any other invalid argument                         */
 };
 
 /* Human-readable name of a status code (static string). */
@@ -69,8 +71,10 @@ BS_API int bs_version(void);
  * load time (radiance_kernels.py page, install_load_hook; radiance_mxfp4.py
  * page, the WPERM comment and permute_w).  It is a byte permutation, not a
  * re-quantisation, and has an exact inverse.  The layout is recorded in a
- * HOST-side descriptor that every GEMM call checks, so a weight in the wrong
- * layout is an error (BS_ERR_LAYOUT), never silently misread.
+ * HOST-side descriptor that every GEMM call checks field by field against
+ * what the pre-layout of its (N, K) writes, so a weight in the wrong layout,
+ * or a descriptor of another shape, is an error (BS_ERR_LAYOUT), never
+ * silently misread.
  *
  * Order: the weight is cut into 16-row tiles and 128-wide K steps.  In each
  * (tile nt, step ks), lane l of a 64-lane wave owns row 16*nt + l%16 and the
@@ -203,8 +207,9 @@ BS_API int bsgemm_w4a8_mxfp4_atiled(const void* a_tiled, const float* a_scale, c
 /* Skinny bf16 NT GEMM (radiance_gemm.py page, gemm_bf16_nt_m64):
  *   C[m,n] = bf16( sum_k x[m,k] * w[n,k] ), fp32 accumulation.
  * x: bf16 [M, K]; w: bf16 [N, K]; c: bf16 [M, N]; all contiguous row-major,
- * 16-byte aligned.  1 <= M <= 64, N % 16 == 0, K % 128 == 0.  K is split
- * across workgroups; ws must hold bs_workspace_bytes(BS_OP_BF16_SKINNY,...). */
+ * 16-byte aligned.  1 <= M <= 64, N % 16 == 0, K >= 32, K % 32 == 0 (K past
+ * the last multiple of 128 runs as a partial chunk).  K is split across
+ * workgroups; ws must hold bs_workspace_bytes(BS_OP_BF16_SKINNY, ...). */
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws,
                             size_t ws_bytes, bs_stream_t stream);
 
@@ -218,7 +223,7 @@ BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N,
  *     M, N, K), exceeds BS_NOALLOC_SCRATCH_BYTES returns BS_ERR_SCRATCH and
  *     launches nothing (e.g. at M = 64: N <= 1600 for K = 5120, N <= 4032 for
  *     K = 2048).
- *   - The stream must belong to the current device (else BS_ERR_ARG).
+ *   - The stream must belong to the current device (else BS_ERR_DEVICE).
  *   - The first call on a device looks up the array's address on that device
  *     and clears its counters with a kernel on the stream; make it outside
  *     graph capture.  After that every call leaves the counters zeroed.

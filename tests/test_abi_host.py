@@ -90,14 +90,24 @@ def test_gemm_argument_validation(blib):
     assert fp8(desc=bad) == -4
     assert fp8(lda=500) == -3
     assert fp8(a=ctypes.c_void_p(0x10008)) == -3
-    assert fp8(asm=-1) == -7
+    assert fp8(asm=-1) == -9
     mx = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 256 * 256, 65536, 4096, 65536 + 4096)
     assert fp8(desc=mx) == -4                      # right shape, wrong layout
+    # every descriptor field must be what the pre-layout of (N, K) writes
+    for bad_fp8 in (WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 512, 256 * 511, 0, 0, 256 * 512),
+                    WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 512, 256 * 512, 0, 4096, 256 * 512),
+                    WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 512, 256 * 512, 0, 0, 256 * 512 - 16)):
+        assert fp8(desc=bad_fp8) == -4
 
     def w4(M=8, N=256, K=512, desc=mx, w=FAKE):
         return blib.bsgemm_w4a8_mxfp4(FAKE, 512, FAKE, ctypes.byref(desc), w, FAKE, 256, M, N, K, None, 0, None)
     assert w4(N=250) == -2
     assert w4(desc=d) == -4
+    for bad_mx in (WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 65536 - 256, 65536, 4096, 65536 + 4096),
+                   WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 65536, 65536 + 256, 4096, 65536 + 4352),
+                   WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 65536, 65536, 2048, 65536 + 2048),
+                   WDesc(BS_WDESC_MAGIC, BS_LAYOUT_MXFP4, 256, 512, 65536, 65536, 4096, 65536)):
+        assert w4(desc=bad_mx) == -4
     assert w4(w=ctypes.c_void_p(0x10010)) == -3   # the pre-laid-out weight must be 256-byte aligned
     # long K splits across workgroups: a missing or short workspace is refused before any launch
     dk = WDesc(BS_WDESC_MAGIC, BS_LAYOUT_FP8_BLOCK, 256, 17408, 256 * 17408, 0, 0, 256 * 17408)
@@ -110,13 +120,15 @@ def test_gemm_argument_validation(blib):
 
 def test_skinny_and_producer_validation(blib):
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 65, 96, 5120, None, 0, None) == -2
-    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5000, None, 0, None) == -2
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5000, None, 0, None) == -2   # K % 32
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 16, None, 0, None) == -2     # K < 32
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5024, None, 0, None) == -5   # K % 32 taken; split
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, None, 0, None) == -5   # K split needs a workspace
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, FAKE, 16, None) == -5
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5121, None) == -2
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 65536, None) == -2
     assert blib.add_rms_quant_fp8(None, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5120, None) == -1
-    assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, 8, 5120, None) == -7
+    assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, FAKE, 8, 5120, None) == -9
     assert blib.add_rms_quant_fp8_group128(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5000,
                                            None) == -2                          # K % 128
     assert blib.silu_mul_quant_fp8(FAKE, FAKE, FAKE, 8, 17404, None) == -2       # N % 8
@@ -132,7 +144,7 @@ def test_prelayout_validation(blib):
     from block_scaled_precision_04_amd._binding import WDesc
     d = WDesc()
     assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 1 << 20, 250, 512, ctypes.byref(d), None) == -2
-    assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 100, 256, 512, ctypes.byref(d), None) == -7   # out too small
+    assert blib.bs_prelayout_fp8_block(FAKE, FAKE, 100, 256, 512, ctypes.byref(d), None) == -9   # out too small
     assert blib.bs_prelayout_mxfp4(FAKE, FAKE, FAKE, 1 << 20, 32, 100, ctypes.byref(d), None) == -2
     assert blib.bs_unprelayout_fp8_block(ctypes.byref(d), FAKE, FAKE, None) == -4             # empty descriptor
 

@@ -351,7 +351,11 @@ def test_skinny_workload(case):
     checks.assert_gemm_close(got, ce, asum, f"skinny M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 32, 384), (33, 48, 640), (64, 16, 128), (5, 1280, 5120)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 32, 384), (33, 48, 640), (64, 16, 128), (5, 1280, 5120),
+                                   # K % 32 == 0 but not a multiple of 128: a partial last chunk,
+                                   # alone (K = 32, 96) and after whole ones, split and unsplit
+                                   (8, 16, 32), (3, 32, 96), (16, 64, 160), (33, 96, 2080), (64, 48, 5024),
+                                   (8, 96, 5216)])
 def test_skinny_edges(M, N, K):
     g = synth.rng(M * 1000 + N + K)
     x = synth.bf16_normal(g, (M, K), 1.0)
