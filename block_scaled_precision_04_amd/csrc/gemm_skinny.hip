@@ -52,13 +52,13 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
     const int k0 = chunk * kChunk + 32 * (l >> 4);
     const bool k_in = k0 < K;
     const int kl = k_in ? k0 : K - 32;
+    // (an and-mask rather than a select, which the compiler turns into a
+    // conditional load and then cannot hoist the activation loads past)
+    const uint32_t keep = k_in ? 0xFFFFFFFFu : 0u;
     const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(nt * 16 + (l & 15)) * K + kl);
     uint4 wv[4], xv[MB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 v = wr[j];
-      wv[j] = k_in ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) wv[j] = wr[j];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = min(16 * mb + (l & 15), M - 1);
@@ -66,6 +66,10 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) xv[mb][j] = xr[j];
     }
+    // every load of the chunk is issued before the first MFMA waits on one
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wv[j] = make_uint4(wv[j].x & keep, wv[j].y & keep, wv[j].z & keep, wv[j].w & keep);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
