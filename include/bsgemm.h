@@ -138,7 +138,14 @@ BS_API int bs_unprelayout_mxfp4(const bs_wdesc* desc, const void* pre, void* w_p
  * shapes, whose bs_workspace_bytes it covers.  Calls that share a workspace
  * must be ordered (same stream); 0 means no workspace is needed.  A split
  * that would need more than 16384 counters (one per 16-column tile group)
- * is refused with BS_ERR_SHAPE. */
+ * is refused with BS_ERR_SHAPE.
+ * Memory kind: ordinary device memory of the GPU the call runs on (hipMalloc,
+ * coarse-grained).  The workgroups of one tile may run on different XCDs,
+ * whose L2 caches are not coherent with each other; the hand-off works
+ * because the partials are written and read with device-scope (sc1) memory
+ * instructions and each workgroup waits for its partial stores to be
+ * acknowledged before it bumps the counter with a device-scope atomic.  The
+ * test suite pins that encoding in the compiled kernels. */
 enum { BS_OP_FP8_BLOCK = 1, BS_OP_W4A8_MXFP4 = 2, BS_OP_BF16_SKINNY = 3 };
 BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
 

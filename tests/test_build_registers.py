@@ -172,3 +172,28 @@ def test_prefill_k_loop_keeps_mfmas_and_loads_interleaved():
         assert interleaved >= 3 * min(half, dma), f"{name}: only {interleaved} MFMAs followed by a load"
         seen += 1
     assert seen == 4, f"{seen} prefill instantiations found"
+
+
+def test_split_k_handoff_uses_device_scope_instructions():
+    seen = 0
+    for src in ("gemm_skinny.hip", "gemm_decode.hip", "gemm_prefill.hip"):
+        for name, ins in _kernels(_asm(src)):
+            atoms = [i for i, s in enumerate(ins) if s.startswith("global_atomic_add")]
+            if not atoms:
+                continue
+            a = atoms[0]
+            stores = [i for i, s in enumerate(ins[:a]) if s.startswith("global_store")]
+            assert stores, f"{name}: no partial store before the counter"
+            # the partial stores are the device-scope ones of the path
+            dev = [i for i in stores if re.search(r"\bsc1\b", ins[i])]
+            assert dev, f"{name}: partial stores without sc1: {[ins[i] for i in stores[-4:]]}"
+            last = dev[-1]
+            waits = [s for s in ins[last + 1:a] if s.startswith("s_waitcnt") and "vmcnt(0)" in s]
+            assert waits, f"{name}: counter bumped before the partial stores are acknowledged"
+            assert "sc0" in ins[a], f"{name}: counter atomic does not return its value: {ins[a]}"
+            loads = [s for s in ins[a + 1:] if s.startswith("global_load") and re.search(r"\bsc1\b", s)]
+            assert loads, f"{name}: the partials are not read back with device-scope loads"
+            assert not any(s.startswith(("buffer_wbl2", "buffer_inv")) for s in ins), \
+                f"{name}: cache maintenance in the hand-off (it costs microseconds per workgroup)"
+            seen += 1
+    assert seen >= 10, f"only {seen} kernels with a split-K hand-off found"
