@@ -12,7 +12,7 @@ size_t bs_decode_workspace(int M, int N, int K, bool mx);
 int bs_launch_fp8_block_prefill(const uint8_t* a, int64_t lda, const float* as, int64_t as_m, int64_t as_g,
                                 const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,
                                 hipStream_t st);
-int bs_fp8_prefill_min_m();
+bool bs_fp8_use_tiled(int M, int N, int K);
 int bs_launch_w4a8_prefill(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w, const uint32_t* wsc,
                            uint16_t* c, int64_t ldc, int M, int N, int K, void* ws, bool a_tiled, hipStream_t st);
 size_t bs_prefill_workspace(int M, int N, int K);
@@ -81,7 +81,7 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K) {
   }
   if (op == BS_OP_FP8_BLOCK) {
     if (M < 1 || M > kFp8MaxM || N < 128 || N % 128 || K < 128 || K % 128) return 0;
-    return M >= bs_fp8_prefill_min_m() ? 0 : bs_decode_workspace(M, N, K, false);
+    return bs_fp8_use_tiled(M, N, K) ? 0 : bs_decode_workspace(M, N, K, false);
   }
   if (op == BS_OP_W4A8_MXFP4) {
     if (M < 1 || M > (1 << 22) || N < 16 || N % 16 || K < 128 || K % 128) return 0;
@@ -109,7 +109,7 @@ BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, in
   // scales (256 * as_stride_m floats) and weight scales ((N/128) * (K/128)
   // floats) with unsigned 32-bit offsets
   BS_CHECK(as_stride_m < (1 << 22), BS_ERR_SHAPE);
-  if (M >= bs_fp8_prefill_min_m()) {
+  if (bs_fp8_use_tiled(M, N, K)) {
     BS_CHECK(lda < (1 << 24) && static_cast<uint64_t>(N / 128) * (K / 128) < (1ull << 30), BS_ERR_SHAPE);
     return bs_launch_fp8_block_prefill(static_cast<const uint8_t*>(a), lda, a_scale, as_stride_m, as_stride_g,
                                        static_cast<const uint8_t*>(w_pre), w_scale, static_cast<uint16_t*>(c), ldc,

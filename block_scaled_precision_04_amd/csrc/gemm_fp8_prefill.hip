@@ -239,9 +239,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
 
 }  // namespace
 
-// Rows at which the tiled kernel takes over from the row-chunked decode
-// kernel (the weight stream is then reused by enough rows to be MFMA-bound).
-int bs_fp8_prefill_min_m() { return 512; }
+// Whether the tiled kernel takes the call instead of the decode kernel, which
+// runs 64 rows per launch and streams the whole weight once per launch.  The
+// tiled kernel sweeps all of K in every 256x256 tile with no split, so below
+// 512 rows it has only ceil(M/256) * N/256 workgroups and its time is about
+// that of one tile's K sweep (75-79 us at K = 5120 for N = 5120 and 10240,
+// ~240 us at K = 17408).  Measured on MI355X against ceil(M/64) decode
+// launches (graph-replayed, pooled weights): at K = 5120 the tiled kernel is
+// faster from M = 384 (N = 5120: 81 -> 75 us; M = 448: 95 -> 76) and from
+// M = 256 at N = 10240 (83 -> 79; M = 448: 142 -> 79); at K = 17408 the
+// decode launches stay faster or equal up to M = 448.  Hence: from 512 rows
+// always, and below that when K has at most 64 steps and the decode
+// launches would stream at least 35840 columns' worth of weight rows
+// (ceil(M/64) * N >= 35840).
+bool bs_fp8_use_tiled(int M, int N, int K) {
+  if (M >= 512) return true;
+  return K / 128 <= 64 && static_cast<int64_t>((M + 63) / 64) * N >= 35840;
+}
 
 int bs_launch_fp8_block_prefill(const uint8_t* a, int64_t lda, const float* as, int64_t as_m, int64_t as_g,
                                 const uint8_t* w, const float* ws, uint16_t* c, int64_t ldc, int M, int N, int K,

@@ -163,13 +163,15 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
  * ws:      bs_workspace_bytes(BS_OP_FP8_BLOCK, M, N, K) bytes (256-byte
  *          aligned, zeroed once) when that is non-zero: K split across
  *          workgroups; otherwise may be NULL.
- * Regimes: M < 512 streams the weight (small M; 64 < M < 512 runs as
- * consecutive 64-row launches on the stream, all sharing ws); M >= 512 runs
- * the LDS-tiled kernel (256x256 tiles), which needs no workspace.
+ * Regimes: small M streams the weight (64 < M runs as consecutive 64-row
+ * launches on the stream, all sharing ws); M >= 512, and from 129 rows up
+ * when K <= 8192 and ceil(M/64) * N >= 35840 (where the repeated weight
+ * stream costs more than the tiled kernel's K sweep), run the LDS-tiled
+ * kernel (256x256 tiles), which needs no workspace.
  * Needs M >= 1, N % 128 == 0, K % 128 == 0, K < 2^24, lda < 2^25,
- * 0 <= as_stride_m < 2^22, as_stride_g >= 0 (and, for M >= 512, lda < 2^24
- * and (N/128)*(K/128) < 2^30); a, c and w_pre 16-byte aligned, the scales
- * 4-byte aligned. */
+ * 0 <= as_stride_m < 2^22, as_stride_g >= 0 (and, in the tiled regime,
+ * lda < 2^24 and (N/128)*(K/128) < 2^30); a, c and w_pre 16-byte aligned,
+ * the scales 4-byte aligned. */
 BS_API int bsgemm_fp8_block(const void* a, int64_t lda, const float* a_scale, int64_t as_stride_m,
                             int64_t as_stride_g, const bs_wdesc* wd, const void* w_pre,
                             const float* w_scale, void* c, int64_t ldc, int M, int N, int K,

@@ -60,6 +60,11 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
     assert blib.bs_workspace_bytes(1, 8, 5120, 17408) > 0     # long K: split across workgroups
     assert blib.bs_workspace_bytes(1, 2048, 5120, 17408) == 0  # large M: the tiled kernel, no split
+    # 64 < M < 512: the tiled kernel only where the repeated weight stream costs more
+    assert blib.bs_workspace_bytes(1, 448, 5120, 5120) == 0    # 7 x 5120 >= 35840, K = 5120
+    assert blib.bs_workspace_bytes(1, 256, 10240, 5120) == 0   # 4 x 10240
+    assert blib.bs_workspace_bytes(1, 320, 5120, 5120) > 0     # 5 x 5120: decode launches
+    assert blib.bs_workspace_bytes(1, 448, 5120, 17408) > 0    # K = 17408: decode launches
     assert blib.bs_workspace_bytes(2, 8, 17408, 17408) > 0
     assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
     assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K

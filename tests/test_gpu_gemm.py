@@ -392,6 +392,23 @@ def test_fp8_block_prefill_edges(M, N, K, colmajor):
     checks.assert_gemm_close(got, ce, asum, f"fp8 block prefill edge M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K,tiled", [(448, 5120, 5120, True), (200, 10240, 5120, True),
+                                         (320, 5120, 5120, False), (448, 5120, 17408, False)])
+def test_fp8_block_mid_m_routing(M, N, K, tiled):
+    """65 <= M < 512: the tiled kernel where ceil(M/64) decode launches would
+    stream the weight more often than it pays (K <= 8192 and
+    ceil(M/64) * N >= 35840), else the 64-row decode launches; the oracle
+    on a grid of the edge rows and columns plus random ones (about two per
+    16-row block and two per 256-column stripe)."""
+    wsb = bs.lib().bs_workspace_bytes(bs.BS_OP_FP8_BLOCK, M, N, K)
+    assert (wsb == 0) == tiled
+    aq, asc, wq, wsc = fp8_block_inputs(12, M + N + K, M, N, K, outliers=True)
+    got = _fp8_run(aq, asc, wq, wsc)
+    rows, cols = sample_grid(M, N, 2 * -(-M // 16), 2 * N // 256, seed=M + N)
+    _, ce, asum = gemm.fp8_block_gemm_at(aq, asc, wq, wsc, rows, cols)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, f"fp8 block mid-M M={M} N={N} K={K}")
+
+
 def test_fp8_block_prefill_no_out_of_bounds_writes_and_ldc():
     M, N, K = 700, 384, 512
     aq, asc, wq, wsc = fp8_block_inputs(9, 11, M, N, K)
