@@ -118,16 +118,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
   const uint32_t soff = static_cast<uint32_t>((min(m0 + wave * 64 + l, M - 1) - m0) * as_m * 4);
   // weight scales of the tile's 128-column blocks: lane j -> block (n0/128 + j)
   const uint32_t woff = static_cast<uint32_t>(min((n0 >> 7) + l, (N >> 7) - 1)) * static_cast<uint32_t>(KS) * 4u;
-  auto dma_stage = [&](int ks, int buf) {
+  // the i-th 16-byte load of stage ks (activation pieces, then weight pieces)
+  auto dma_piece = [&](int i, int ks, int buf) {
     const uint32_t base = lds0 + buf * kStage;
-#pragma unroll
-    for (int i = 0; i < kAIters; ++i) dma16(base + (i * kWaves + wave) * 1024, a_tile + ks * 128, aoff[i]);
-#pragma unroll
-    for (int j = 0; j < kBIters; ++j)
+    if (i < kAIters) {
+      dma16(base + (i * kWaves + wave) * 1024, a_tile + ks * 128, aoff[i]);
+    } else {
+      const int j = i - kAIters;
       dma16(base + kAStage + (j * kWaves + wave) * 1024, w_tile + static_cast<size_t>(ks) * 2048, boff[j]);
+    }
+  };
+  auto dma_scales = [&](int ks, int buf) {
+    const uint32_t base = lds0 + buf * kStage;
     if (wave < kSWaves) dma4(base + kAStage + kBStage + wave * 256, as_tile + ks * as_g, soff);
     else if (wave == kSWaves) dma4(base + kAStage + kBStage + kSStage, wsc + ks, woff);
   };
+  auto dma_stage = [&](int ks, int buf) {
+#pragma unroll
+    for (int i = 0; i < kAIters + kBIters; ++i) dma_piece(i, ks, buf);
+    dma_scales(ks, buf);
+  };
+  static_assert(kAIters + kBIters == kNB, "one load of the next stage per 16-column block");
 
   // ---- fragment offsets within a stage.  Both operands hold K = 32*(l/16)
   // .. +31 of their row in lane l (the pre-layout's order; the pairing inside
@@ -162,9 +173,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
 
   for (int ks = 0; ks < KS; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < KS) dma_stage(ks + 1, buf ^ 1);
-
-    if (live_n) {
+    // The next stage's loads go out one per 16-column block, between the
+    // MFMAs, rather than as a burst before them: a burst of 17 loads per wave
+    // (136 per workgroup) backs up the load unit, and each wave stalls on it
+    // before its first MFMA.  After the last step they reload the last stage
+    // into the idle buffer (never read).
+    const int kn = min(ks + 1, KS - 1);
+    dma_scales(kn, buf ^ 1);
+    if (!live_n) {
+#pragma unroll
+      for (int i = 0; i < kAIters + kBIters; ++i) dma_piece(i, kn, buf ^ 1);
+    } else {
       const uint8_t* st = lds + buf * kStage;
       float s[kMB];
       v8i af[kMB];
@@ -187,6 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
         v4f tn[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) tn[mb] = mfma_group(bcur, af[mb]);
+        dma_piece(nb, kn, buf ^ 1);
         if (nb > 0) {
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) acc[mb][nb - 1] += t[mb] * s[mb];
