@@ -213,13 +213,22 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = v4f{0, 0, 0, 0};
   // Lanes whose row is past M compute garbage in their own output column only
-  // (never stored), so only the steps past this wave's range need masking: a
-  // wave-uniform branch.
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r >= nsteps) break;
-    v8i af[MB];
-    float sa[MB];
+  // (never stored), so only the steps past this wave's range need care.
+  // Where two fragment sets fit in 128 VGPRs (four waves per SIMD), the
+  // fragments of step r+1 are read from LDS before the MFMAs of step r, so
+  // the LDS latency runs under them.  That form runs every step and zeroes
+  // the products of those past the range (MXFP4: the weight fragment;
+  // block-FP8: the step's scale), which meet clamped re-reads of this wave's
+  // last step: an and-mask, because with a branch per step the compiler sinks
+  // the MFMAs below the branches and the read-ahead is lost.  Otherwise each
+  // step reads its own fragments just before its MFMAs and the loop ends at
+  // the range's end (the mask-and-run form costs these registers: M = 64
+  // block-FP8 with 8 tiles of 8 steps went from 123 to 129 VGPRs).
+  constexpr bool kPipeA = T * R * (MX ? 4 : 8) + 2 * MB * (MX ? 8 : 9) + T * MB * 4 + 16 <= 128;
+  constexpr int kSets = kPipeA ? 2 : 1;
+  v8i af[kSets][MB];
+  float sa[kSets][MB];
+  auto read_a = [&](int r, v8i (&f)[MB], float (&sf)[MB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int rc = min(16 * mb + (l & 15), RS - 1);
@@ -227,24 +236,41 @@ __global__ __launch_bounds__(TW * KW * 64) void k_decode(DecodeArgs p) {
       const uint8_t* rb = lds + ((kw * R + r) * RS + rc) * 128;
       const uint4 x = *reinterpret_cast<const uint4*>(rb + ((c0 ^ a_swz(rc)) << 4));
       const uint4 y = *reinterpret_cast<const uint4*>(rb + ((c1 ^ a_swz(rc)) << 4));
-      af[mb] = pack8(x, y);
-      if constexpr (!MX) sa[mb] = s_as[(kw * R + r) * RS + rc];
+      f[mb] = pack8(x, y);
+      if constexpr (!MX) sf[mb] = s_as[(kw * R + r) * RS + rc];
     }
+  };
+  if constexpr (kPipeA) read_a(0, af[0], sa[0]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int cur = kPipeA ? (r & 1) : 0;
+    if constexpr (kPipeA) {
+      if (r + 1 < R) read_a(r + 1, af[(r + 1) & 1], sa[(r + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (r >= nsteps) break;
+      read_a(r, af[0], sa[0]);
+    }
+    const int live = kPipeA && r >= nsteps ? 0 : -1;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if constexpr (MX) {
         const int sc = static_cast<int>(sd[t][r >> 2] >> (8 * (r & 3)));
+        const v8i wm = wf[t][r] & live;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[t][mb] = mfma_fp4w_fp8a(wf[t][r], af[mb], acc[t][mb], sc);
+        for (int mb = 0; mb < MB; ++mb) acc[t][mb] = mfma_fp4w_fp8a(wm, af[cur][mb], acc[t][mb], sc);
       } else {
-        const float sw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsv), t * R + r));
+        // (block-FP8 scales each product anyway: a zero scale drops the step)
+        const float sw =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsv), t * R + r) & live);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const v4f tmp = mfma_fp8(wf[t][r], af[mb], v4f{0, 0, 0, 0});
-          acc[t][mb] += tmp * (sa[mb] * sw);
+          const v4f tmp = mfma_fp8(wf[t][r], af[cur][mb], v4f{0, 0, 0, 0});
+          acc[t][mb] += tmp * (sa[cur][mb] * sw);
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- 4. add the KW partials of each tile in kw order ----------------------
