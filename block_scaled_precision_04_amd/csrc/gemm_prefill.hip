@@ -95,7 +95,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     float* __restrict__ slab, int* __restrict__ counters) {
   using C = PrefillCfg<BM, BN, WM, WN>;
   constexpr int STAGES = 3;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage];
+  // the stage buffers, then the tile's BM per-token activation scales
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * C::kStage + BM * 4];
   __shared__ int last;
   const int S = SPLIT ? static_cast<int>(gridDim.y) : 1, sp = SPLIT ? static_cast<int>(blockIdx.y) : 0;
   const int k_begin = SPLIT ? KS * sp / S : 0;   // KS < 2^24 (K < 2^31), so KS * S fits in 32 bits
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   const int KQ = (KS + 3) >> 2;
   const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const float* s_tok = reinterpret_cast<const float*>(lds + STAGES * C::kStage);
   int mt, ntile;
   xcd_tile(blockIdx.x, m_tiles, n_tiles, group_m, mt, ntile);
   const int m0 = mt * BM, n0 = ntile * BN;
@@ -315,6 +317,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     for (int i = C::kTN * C::kTM; i < C::kDma; ++i)
       if (DMA) dma_one(i, dks, dbuf);
   };
+  // The tile's per-token scales go to LDS ahead of the first stage (64 rows
+  // per wave-wide 4-byte load; with BM < 256 the waves past BM / 64 repeat an
+  // earlier wave's load), so the epilogue does not wait on global loads.
+  {
+    constexpr int kTokLoads = BM / 64;
+    static_assert(BM % 64 == 0 && kTokLoads <= C::kWaves, "one 64-row scale load per wave");
+    const int part = wave % kTokLoads;
+    dma4(lds0 + STAGES * C::kStage + part * 256, as,
+         static_cast<uint32_t>(min(m0 + part * 64 + l, M - 1)) * 4u);
+  }
 #pragma unroll
   for (int i = 0; i < C::kDma; ++i) dma_one(i, k_begin, 0);
 #pragma unroll
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
 #pragma unroll
     for (int q = 0; q < C::kTM; ++q) {
       const int r = arow[q];
-      const float sc = as[min(m0 + r, M - 1)];
+      const float sc = s_tok[r];
 #pragma unroll
       for (int p = 0; p < C::kTN; ++p) {
 #pragma unroll
@@ -444,13 +456,40 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
       constexpr int kRows2 = C::kThreads / kPairs;
       static_assert(C::kThreads % kPairs == 0 && BM % kRows2 == 0, "wide store pass shape");
       const int j = tid % kPairs, r0 = tid / kPairs;
-      const bool n_ok = n0 + 8 * j < N;  // N % 16 == 0: a 16-byte piece is wholly inside or outside
+      if (m0 + BM <= M && n0 + BN <= N) {
+        // whole tile (wave-uniform test): no per-row guard, the row address
+        // advances by a scalar stride, and the LDS reads of a batch are all
+        // issued before its stores (kRows2 is even, so r % 2 == r0 % 2)
+        constexpr int kIters = BM / kRows2, kBatch = 8;
+        static_assert(kRows2 % 2 == 0 && kIters % kBatch == 0, "store batch shape");
+        // odd rows hold each pair's two 8-byte halves swapped: undone with a
+        // per-lane bit mask (a select on the whole vector compiles to
+        // exec-masked moves, each waiting for its LDS read)
+        const uint32_t odd = (r0 & 1) ? 0xFFFFFFFFu : 0u;
+        auto pick = [odd](uint32_t x, uint32_t y) { return (x & ~odd) | (y & odd); };
+        uint16_t* crow = c + (m0 + r0) * ldc + n0 + 8 * j;
+        const int64_t rstep = kRows2 * ldc;
+#pragma unroll
+        for (int b0 = 0; b0 < kIters; b0 += kBatch) {
+          uint4 o[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int r = r0 + (b0 + u) * kRows2;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + (j ^ ((r & 31) >> 1)) * 16);
+            o[u] = make_uint4(pick(v.x, v.z), pick(v.y, v.w), pick(v.z, v.x), pick(v.w, v.y));
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) st_stream16(reinterpret_cast<uint4*>(crow + (b0 + u) * rstep), o[u]);
+        }
+      } else {
+        const bool n_ok = n0 + 8 * j < N;  // N % 16 == 0: a 16-byte piece is wholly inside or outside
 #pragma unroll 4
-      for (int r = r0; r < BM; r += kRows2) {
-        const int s = r & 31;
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + (j ^ (s >> 1)) * 16);
-        const uint4 o = (s & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
-        if (n_ok && m0 + r < M) st_stream16(reinterpret_cast<uint4*>(c + (m0 + r) * ldc + n0 + 8 * j), o);
+        for (int r = r0; r < BM; r += kRows2) {
+          const int s = r & 31;
+          const uint4 v = *reinterpret_cast<const uint4*>(lds + r * (BN * 2) + (j ^ (s >> 1)) * 16);
+          const uint4 o = (s & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
+          if (n_ok && m0 + r < M) st_stream16(reinterpret_cast<uint4*>(c + (m0 + r) * ldc + n0 + 8 * j), o);
+        }
       }
     } else {
       const int j = tid % kPieces, r0 = tid / kPieces;
