@@ -248,6 +248,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
     }
   }
   __syncthreads();
+  if (m0 + kBM <= M && n0 + kBN <= N && ldc % 8 == 0) {
+    // whole tile, 16-byte rows (wave-uniform test): the swizzle moves pieces
+    // in groups of four, so pieces 2p and 2p+1 stay adjacent and in order;
+    // lane p of a row stores pair p, the row address advances by a scalar
+    // stride and a batch's LDS reads are issued before its stores
+    constexpr int kPairs = kBN / 8, kRows2 = kThreads / kPairs, kIters = kBM / kRows2, kBatch = 8;
+    static_assert(kThreads % kPairs == 0 && kIters % kBatch == 0, "store batch shape");
+    const int p = tid % kPairs, r0 = tid / kPairs;
+    uint16_t* crow = c + static_cast<int64_t>(m0 + r0) * ldc + n0 + 8 * p;
+    const int64_t rstep = kRows2 * ldc;
+#pragma unroll
+    for (int b0 = 0; b0 < kIters; b0 += kBatch) {
+      uint4 o[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int r = r0 + (b0 + u) * kRows2;
+        o[u] = *reinterpret_cast<const uint4*>(lds + r * (kBN * 2) + ((2 * p) ^ ((r & 7) << 2)) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) st_stream16(reinterpret_cast<uint4*>(crow + (b0 + u) * rstep), o[u]);
+    }
+    return;
+  }
   const int j = tid % kPieces, r0 = tid / kPieces;
   const bool n_ok = n0 + 4 * j < N;
 #pragma unroll 4
