@@ -28,7 +28,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Workgroup reductions over W waves (wave partials through LDS, added in wave order).
+// Workgroup reductions over W waves (wave partials through LDS, added in wave
+// order).  Each LDS array serves one reduction per kernel, so no barrier
+// follows the reads.
 template <int W = kThreads / 64>
 BS_INLINE float block_max(float v, float* red) {
   v = wave_max(v);
@@ -38,7 +40,6 @@ BS_INLINE float block_max(float v, float* red) {
   float r = red[0];
 #pragma unroll
   for (int i = 1; i < W; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
   return r;
 }
 
@@ -56,7 +57,6 @@ BS_INLINE double block_sum_f64(double v, double* red) {
 #pragma unroll
     for (int i = 1; i < W; ++i) r += red[i];
   }
-  __syncthreads();
   return r;
 }
 
@@ -481,6 +481,22 @@ int launch_row_quant(const void* y, const void* res, const void* gamma, float ep
     else if (nc <= 4) BS_ROWQ128(4);
     else BS_ROWQ128(5);
 #undef BS_ROWQ128
+    return bs_launch_status();
+  }
+  if (GROUP && M < 256 && K / 8 > kThreads) {
+    // group scales, fewer rows than CUs: 1024 threads per row, so each thread
+    // carries at most a few chunks through the serial per-element arithmetic
+    // (M = 8, K = 5120: 4.34 -> 4.18 us; the per-row-scale form, whose block
+    // maximum then spans 16 waves, went from 4.24 to 4.75 us)
+    const int nc = (K / 8 + 1023) / 1024;
+#define BS_ROWQ1K(N_)                                                                                   \
+  k_row_quant<N_, NORM, GROUP, 1024, TILED><<<dim3(M), dim3(1024), 0, st>>>(                           \
+      static_cast<const uint4*>(y), static_cast<const uint4*>(res), static_cast<const uint4*>(gamma), eps, \
+      static_cast<uint2*>(q), scale, static_cast<uint4*>(rout), K)
+    if (nc <= 1) BS_ROWQ1K(1);
+    else if (nc <= 2) BS_ROWQ1K(2);
+    else BS_ROWQ1K(4);
+#undef BS_ROWQ1K
     return bs_launch_status();
   }
   const int nc = (K / 8 + kThreads - 1) / kThreads;
