@@ -88,9 +88,11 @@ struct PrefillCfg {
 // one 32x32x64 MFMA operand, written so by the tiled producer).  A stage's
 // activation tile is then BM/32 contiguous 4 KiB blocks, copied as they are,
 // and a fragment is read at a fixed lane offset: no swizzle, no re-layout.
-template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT = false>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
-    const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
+// The work of one output tile, bx (the tile's position in the launch order);
+// the kernel below runs it for one tile or, for the large tiles, two.
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT>
+__device__ __forceinline__ void prefill_tile(
+    int bx, const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m,
     float* __restrict__ slab, int* __restrict__ counters) {
   using C = PrefillCfg<BM, BN, WM, WN>;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const float* s_tok = reinterpret_cast<const float*>(lds + STAGES * C::kStage);
   int mt, ntile;
-  xcd_tile(blockIdx.x, m_tiles, n_tiles, group_m, mt, ntile);
+  xcd_tile(bx, m_tiles, n_tiles, group_m, mt, ntile);
   const int m0 = mt * BM, n0 = ntile * BN;
   const int nt0 = n0 >> 4;
 
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   // device-scope stores and loads, no cache maintenance -- the same hand-off
   // as the decode GEMMs.
   auto slot = [&](int b, int p, int q) {
-    const size_t t = ((static_cast<size_t>(b) * gridDim.x + blockIdx.x) * C::kWaves + wave) * C::kTN + p;
+    const size_t t = ((static_cast<size_t>(b) * gridDim.x + bx) * C::kWaves + wave) * C::kTN + p;
     return slab + (t * C::kTM + q) * 1024 + l;
   };
 #pragma unroll
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
   asm volatile("" ::: "memory");
   __syncthreads();
   if (tid == 0)
-    last = __hip_atomic_fetch_add(&counters[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    last = __hip_atomic_fetch_add(&counters[bx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
   if (!last) return;
   {
@@ -544,7 +546,35 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
         for (int r = 0; r < 16; ++r) acc[p][q][r] = tot[(p * C::kTM + q) * 16 + r];
   }
   store_tile();
-  if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&counters[bx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup per output tile, except that a large-tile grid of at least
+// two whole rounds (one workgroup per CU, 256 per round) runs with fewer
+// workgroups than tiles: workgroup b takes tile b and then tile b + G (G the
+// grid size; the first workgroups of the grid get the second tiles, so no
+// round is partial, and G is a multiple of 256, so both tiles belong to the
+// same XCD's share of the tile order).  The second tile starts while the
+// first one's stores are still draining, instead of after the workgroup
+// has ended and a new one has been dispatched.  Split launches (grid
+// (tiles, S)) always run one tile per workgroup.
+template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT = false>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
+    const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
+    const uint8_t* __restrict__ wsc, uint16_t* __restrict__ c, int64_t ldc, int M, int N, int KS, int group_m,
+    float* __restrict__ slab, int* __restrict__ counters) {
+  prefill_tile<BM, BN, WM, WN, OCC, SPLIT, IL, AT>(blockIdx.x, a, lda, as, w, wsc, c, ldc, M, N, KS, group_m, slab,
+                                                   counters);
+  if constexpr (IL && !SPLIT) {
+    // (two inlined copies rather than a loop: the loop kept state across
+    // tiles and spilled)
+    const int second = static_cast<int>(blockIdx.x + gridDim.x);
+    if (second < ((M + BM - 1) / BM) * ((N + BN - 1) / BN)) {
+      __syncthreads();  // every wave is done with the first tile's LDS
+      prefill_tile<BM, BN, WM, WN, OCC, SPLIT, IL, AT>(second, a, lda, as, w, wsc, c, ldc, M, N, KS, group_m, slab,
+                                                       counters);
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT>
@@ -558,7 +588,9 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
     counters = static_cast<int*>(ws);
     slab = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kWsCounterBytes);
   }
-  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL, AT><<<dim3(tiles, S), 64 * WM * WN, 0, st>>>(
+  // large tiles: the first (tiles / 512) * 256 workgroups take two tiles
+  const int grid = IL && !SPLIT ? tiles - (tiles / 512) * 256 : tiles;
+  k_w4a8_prefill<BM, BN, WM, WN, OCC, SPLIT, IL, AT><<<dim3(grid, S), 64 * WM * WN, 0, st>>>(
       a, static_cast<int>(lda), as, w, wsc, c, ldc, M, N, KS, group_m, slab, counters);
   return bs_launch_status();
 }
