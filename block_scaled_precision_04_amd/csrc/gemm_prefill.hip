@@ -76,13 +76,15 @@ struct PrefillCfg {
   static_assert(kTM >= 1 && kTN >= 1, "wave tile too small");
 };
 
-// One workgroup per output tile.  Workgroup b runs on XCD b % 8; the tile
-// sequence is cut into eight contiguous chunks, one per XCD, so the
-// workgroups resident on one XCD at any moment are neighbours in the grouped
-// raster and share activation / weight tiles in that XCD's L2.
-// grid (tiles, S): workgroup (x, y) computes tile x over the y-th of S equal
-// runs of K steps; with S > 1 the partial tile goes to the workspace slab and
-// the last of the S workgroups of a tile adds them in split order.
+// Tile position b is computed by workgroup b, or (large tiles, see the
+// kernel) by workgroup b - G, which runs on the same XCD: workgroup b runs
+// on XCD b % 8 and G is a multiple of 256.  The tile sequence is cut into
+// eight contiguous chunks, one per XCD, so the tiles resident on one XCD at
+// any moment are neighbours in the grouped raster and share activation /
+// weight tiles in that XCD's L2.
+// Split launches, grid (tiles, S): workgroup (x, y) computes tile x over the
+// y-th of S equal runs of K steps; the partial tile goes to the workspace
+// slab and the last of the S workgroups of a tile adds them in split order.
 // AT = true: the activation arrives in the activation-tiled order (32-row
 // blocks of 4 KiB per K step, each half step the 32 bytes of every lane of
 // one 32x32x64 MFMA operand, written so by the tiled producer).  A stage's
