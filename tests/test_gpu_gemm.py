@@ -319,6 +319,32 @@ def test_w4a8_large_tiles_strided_out():
     checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 large tiles strided out")
 
 
+def test_w4a8_two_tile_workgroups_ragged_strided():
+    """Large-tile grids of two or more rounds run two tiles per workgroup:
+    M=4196 (17 row tiles, the last 100 rows deep), N=8240 (33 column tiles,
+    the last 48 wide) is 561 large tiles with no column strip, so workgroups
+    0..255 take tiles b and b + 305.  Written into a strided view inside a
+    guard frame (whole tiles take the 16-byte store path, ragged ones the
+    guarded path): nothing outside the view changes, and one element of
+    every 128x128 cell plus the tile seams match the oracle."""
+    M, N, K = 4196, 8240, 1024
+    assert (M + 255) // 256 * ((N + 255) // 256) == 561
+    assert bs.workspace_bytes(bs.BS_OP_W4A8_MXFP4, M, N, K) == 0      # one unsplit launch
+    aq, asc, wp, e = w4a8_inputs(8, 29, M, N, K)
+    big, view = _guarded(M, N)
+    _w4_run(aq, asc, wp, e, out=view)
+    assert _frame_untouched(big, M, N)
+    got = host_bits16(view.contiguous())
+    rows, cols = sample_grid(M, N, 12, 24, seed=29)
+    br, bc = block_samples(M, N, 128, seed=30)
+    rr, cc = np.meshgrid(np.array([0, 255, 256, 4095, 4096, M - 1]), np.array([0, 8191, 8192, N - 1]),
+                         indexing="ij")
+    rows = np.r_[rows, br, rr.reshape(-1)]
+    cols = np.r_[cols, bc, cc.reshape(-1)]
+    ce, asum = oracle_at(gemm.w4a8_mxfp4_gemm_at, rows, cols, aq, asc, wp, e)
+    checks.assert_gemm_close(got[rows, cols], ce, asum, "w4a8 two-tile workgroups ragged strided")
+
+
 def test_determinism():
     M, N, K = 256, 1280, 5120
     aq, asc, wp, e = w4a8_inputs(8, 2, M, N, K)
