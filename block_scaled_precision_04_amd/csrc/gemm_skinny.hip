@@ -32,6 +32,8 @@ BS_INLINE v8bf as_bf(uint4 x) {
   v4i t{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
   return __builtin_bit_cast(v8bf, t);
 }
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+BS_INLINE v2bf as_bf2(uint32_t x) { return __builtin_bit_cast(v2bf, x); }
 
 template <int MB>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
@@ -119,9 +121,74 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
   if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Up to 8 rows: one output column per workgroup over the whole of K, dot
+// products on the VALU (v_dot2 over packed bf16 pairs, fp32 sums), so there
+// is no split-K hand-off (graph-replayed, pooled weights: M = 6 / 8,
+// W[256, 2048] 4.46-4.64 -> 3.98-4.01 us, W[96, 5120] 4.97 -> 4.81-4.86 us;
+// at 16 rows each workgroup's activation stream made it slower than the
+// split MFMA form, 4.7 -> 5.8 and 5.3 -> 7.5 us).  Thread t takes the 16-byte chunks t, t + T, ... of
+// the weight row and of each activation row; all NCH chunks' loads are
+// issued before any arithmetic (chunk indices past K re-read the last chunk
+// and are zeroed afterwards), then each row's sum goes through a wave
+// reduction and the T/64 wave partials are added in wave order.
+template <int MR, int T, int NCH>
+__global__ __launch_bounds__(T) void k_skinny_dot(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                  uint16_t* __restrict__ c, int M, int N, int K) {
+  constexpr int kW = T / 64;
+  __shared__ float red[kW][MR];
+  const int n = blockIdx.x;
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63;
+  const int nch = K >> 3;
+  const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(n) * K);
+  uint4 wv[NCH], xv[NCH][MR];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int ch = min(t + j * T, nch - 1);
+    wv[j] = wr[ch];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      xv[j][m] = reinterpret_cast<const uint4*>(x + static_cast<size_t>(min(m, M - 1)) * K)[ch];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const uint32_t keep = t + j * T < nch ? 0xFFFFFFFFu : 0u;
+    const uint4 wk = make_uint4(wv[j].x & keep, wv[j].y & keep, wv[j].z & keep, wv[j].w & keep);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      acc[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wk.x), as_bf2(xv[j][m].x), acc[m], false);
+      acc[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wk.y), as_bf2(xv[j][m].y), acc[m], false);
+      acc[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wk.z), as_bf2(xv[j][m].z), acc[m], false);
+      acc[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(wk.w), as_bf2(xv[j][m].w), acc[m], false);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = acc[m];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (l == 0) red[wave][m] = v;
+  }
+  __syncthreads();
+  if (t < MR && t < M) {
+    float s = red[0][t];
+#pragma unroll
+    for (int i = 1; i < kW; ++i) s += red[i][t];
+    c[static_cast<size_t>(t) * N + n] = static_cast<uint16_t>(bf16x2_rne(s, 0.0f));
+  }
+}
+
 }  // namespace
 
 int bs_skinny_ksplit(int K) { return ((K + kChunk - 1) / kChunk + kWaves - 1) / kWaves; }
+
+namespace {
+// whether the VALU form (one column per workgroup, no split) takes the call
+bool skinny_dot(int M, int K) { return M <= 8 && K <= 8192; }
+}  // namespace
 
 namespace {
 int skinny_mb(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
@@ -132,12 +199,21 @@ size_t skinny_slab_bytes(int M, int N, int ks) {
 
 size_t bs_skinny_workspace(int M, int N, int K) {
   const int ks = bs_skinny_ksplit(K);
-  if (ks <= 1) return 0;
+  if (ks <= 1 || skinny_dot(M, K)) return 0;
   return kWsCounterBytes + skinny_slab_bytes(M, N, ks);
 }
 
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
                      hipStream_t st) {
+  if (skinny_dot(M, K)) {
+    // 16-byte chunks per row: up to 256 on 256 threads, else 512 threads
+    const int nch = K / 8;
+#define BS_DOT(MR_, T_, NCH_) k_skinny_dot<MR_, T_, NCH_><<<dim3(N), dim3(T_), 0, st>>>(x, w, c, M, N, K)
+    if (nch <= 256) BS_DOT(8, 256, 1);
+    else BS_DOT(8, 512, 2);
+#undef BS_DOT
+    return bs_launch_status();
+  }
   const int ks = bs_skinny_ksplit(K);
   float* slab = nullptr;
   int* counters = nullptr;

@@ -69,7 +69,8 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
     assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K
     assert blib.bs_workspace_bytes(1, 8, 100, 5120) == 0      # N % 128 != 0 -> 0
-    assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0
+    assert blib.bs_workspace_bytes(3, 8, 96, 5120) == 0       # skinny, 8 rows: one workgroup per column, no split
+    assert blib.bs_workspace_bytes(3, 16, 96, 5120) > 0       # 16 rows: split K
     assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
 
 
@@ -127,9 +128,11 @@ def test_skinny_and_producer_validation(blib):
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 65, 96, 5120, None, 0, None) == -2
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5000, None, 0, None) == -2   # K % 32
     assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 16, None, 0, None) == -2     # K < 32
-    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5024, None, 0, None) == -5   # K % 32 taken; split
-    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, None, 0, None) == -5   # K split needs a workspace
-    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 8, 96, 5120, FAKE, 16, None) == -5
+    # (16 rows: the split form, which needs a workspace; up to 8 rows take no
+    # workspace, so no call with these fake pointers may pass validation)
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 16, 96, 5024, None, 0, None) == -5  # K % 32 taken; split
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 16, 96, 5120, None, 0, None) == -5  # K split needs a workspace
+    assert blib.gemm_bf16_skinny(FAKE, FAKE, FAKE, 16, 96, 5120, FAKE, 16, None) == -5
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5121, None) == -2
     assert blib.add_rms_quant_fp8(FAKE, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 65536, None) == -2
     assert blib.add_rms_quant_fp8(None, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, FAKE, 8, 5120, None) == -1

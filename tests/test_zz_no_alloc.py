@@ -30,10 +30,10 @@ def _both(x, w):
     return host_bits16(got), host_bits16(ref)
 
 
-@pytest.mark.parametrize("first,second", [((64, 256, 5120), (8, 96, 2048)),     # split K both times
-                                          ((32, 1600, 5120), (6, 256, 2048)),   # near the scratch limit first
-                                          ((16, 96, 5120), (3, 16, 128)),       # then one K chunk (no split)
-                                          ((33, 96, 5216), (8, 48, 2080))])     # K % 128 != 0: partial chunks
+@pytest.mark.parametrize("first,second", [((64, 256, 5120), (12, 96, 2048)),    # split K both times
+                                          ((32, 1600, 5120), (10, 256, 2048)),  # near the scratch limit first
+                                          ((16, 96, 5120), (3, 16, 128)),       # then up to 8 rows (no scratch)
+                                          ((33, 96, 5216), (9, 48, 2080))])     # K % 128 != 0: partial chunks
 def test_noalloc_matches_workspace_entry_point(first, second):
     for i, (M, N, K) in enumerate((first, second)):
         x, w = _inputs(100 * M + N + K + i, M, N, K)
