@@ -121,12 +121,13 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
   if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Up to 8 rows: one output column per workgroup over the whole of K, dot
-// products on the VALU (v_dot2 over packed bf16 pairs, fp32 sums), so there
-// is no split-K hand-off (graph-replayed, pooled weights: M = 6 / 8,
-// W[256, 2048] 4.46-4.64 -> 3.98-4.01 us, W[96, 5120] 4.97 -> 4.81-4.86 us;
-// at 16 rows each workgroup's activation stream made it slower than the
-// split MFMA form, 4.7 -> 5.8 and 5.3 -> 7.5 us).  Thread t takes the 16-byte chunks t, t + T, ... of
+// Up to 8 rows and K <= 2048: one output column per workgroup over the whole
+// of K, dot products on the VALU (v_dot2 over packed bf16 pairs, fp32 sums),
+// so there is no split-K hand-off (M = 6 / 8, W[256, 2048]: 4.46-4.64 ->
+// 3.98-4.01 us graph-replayed over pooled weights, 7.3-7.4 -> 6.5-6.7 us
+// inside the bench step).  Past that each workgroup streams too much of the
+// activation: W[96, 5120] at 8 rows ran 0.2-0.4 us slower inside the bench
+// step (3% faster alone), and at 16 rows W[256, 2048] went from 4.7 to 5.8 us.  Thread t takes the 16-byte chunks t, t + T, ... of
 // the weight row and of each activation row; all NCH chunks' loads are
 // issued before any arithmetic (chunk indices past K re-read the last chunk
 // and are zeroed afterwards), then each row's sum goes through a wave
@@ -187,7 +188,7 @@ int bs_skinny_ksplit(int K) { return ((K + kChunk - 1) / kChunk + kWaves - 1) / 
 
 namespace {
 // whether the VALU form (one column per workgroup, no split) takes the call
-bool skinny_dot(int M, int K) { return M <= 8 && K <= 8192; }
+bool skinny_dot(int M, int K) { return M <= 8 && K <= 2048; }
 }  // namespace
 
 namespace {
@@ -206,12 +207,8 @@ size_t bs_skinny_workspace(int M, int N, int K) {
 int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, int N, int K, void* ws,
                      hipStream_t st) {
   if (skinny_dot(M, K)) {
-    // 16-byte chunks per row: up to 256 on 256 threads, else 512 threads
-    const int nch = K / 8;
-#define BS_DOT(MR_, T_, NCH_) k_skinny_dot<MR_, T_, NCH_><<<dim3(N), dim3(T_), 0, st>>>(x, w, c, M, N, K)
-    if (nch <= 256) BS_DOT(8, 256, 1);
-    else BS_DOT(8, 512, 2);
-#undef BS_DOT
+    // K <= 2048: at most 256 16-byte chunks per row, one per thread
+    k_skinny_dot<8, 256, 1><<<dim3(N), dim3(256), 0, st>>>(x, w, c, M, N, K);
     return bs_launch_status();
   }
   const int ks = bs_skinny_ksplit(K);

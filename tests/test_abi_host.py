@@ -69,8 +69,9 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
     assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K
     assert blib.bs_workspace_bytes(1, 8, 100, 5120) == 0      # N % 128 != 0 -> 0
-    assert blib.bs_workspace_bytes(3, 8, 96, 5120) == 0       # skinny, 8 rows: one workgroup per column, no split
-    assert blib.bs_workspace_bytes(3, 16, 96, 5120) > 0       # 16 rows: split K
+    assert blib.bs_workspace_bytes(3, 8, 256, 2048) == 0      # skinny, 8 rows, K <= 2048: one workgroup per column
+    assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0        # longer K: split
+    assert blib.bs_workspace_bytes(3, 16, 256, 2048) > 0      # 16 rows: split
     assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
 
 

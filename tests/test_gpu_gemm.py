@@ -382,10 +382,9 @@ def test_skinny_workload(case):
                                    # alone (K = 32, 96) and after whole ones, split and unsplit
                                    (8, 16, 32), (3, 32, 96), (16, 64, 160), (33, 96, 2080), (64, 48, 5024),
                                    (8, 96, 5216),
-                                   # up to 8 rows, one workgroup per column: 256 threads (K <= 2048),
-                                   # 512 threads with idle chunk slots (K = 2080), K = 8192 (all slots),
-                                   # and K = 8224 (past that form: the split MFMA kernel)
-                                   (6, 48, 2080), (8, 32, 8192), (7, 16, 8224)])
+                                   # up to 8 rows, one workgroup per column up to K = 2048 (all chunk
+                                   # slots used at 2048, idle ones below); just past it, the split form
+                                   (8, 64, 2048), (2, 16, 1056), (6, 48, 2080), (8, 32, 8192)])
 def test_skinny_edges(M, N, K):
     g = synth.rng(M * 1000 + N + K)
     x = synth.bf16_normal(g, (M, K), 1.0)
