@@ -556,10 +556,11 @@ __device__ __forceinline__ void prefill_tile(
 // workgroups than tiles: workgroup b takes tile b and then tile b + G (G the
 // grid size; the first workgroups of the grid get the second tiles, so no
 // round is partial, and G is a multiple of 256, so both tiles belong to the
-// same XCD's share of the tile order).  The second tile starts while the
-// first one's stores are still draining, instead of after the workgroup
-// has ended and a new one has been dispatched.  Split launches (grid
-// (tiles, S)) always run one tile per workgroup.
+// same XCD's share of the tile order).  The second tile's first loads go
+// out while the first one's stores are still draining (its first wait
+// covers both), instead of after the workgroup has ended and a new one has
+// been dispatched.  Split launches (grid (tiles, S)) always run one tile per
+// workgroup.
 template <int BM, int BN, int WM, int WN, int OCC, bool SPLIT, bool IL, bool AT = false>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void k_w4a8_prefill(
     const uint8_t* __restrict__ a, int lda, const float* __restrict__ as, const uint8_t* __restrict__ w,
