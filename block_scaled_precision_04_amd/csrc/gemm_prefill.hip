@@ -677,11 +677,23 @@ int launch_plan(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w
   // a small-tile launch over columns [n0, n1): the weight's n-tiles from
   // n0 / 16 on (codes KS KiB and scales ceil(KS/4) * 256 bytes per
   // 16-column tile), output columns from n0 on
+  // More small-tile workgroups than CUs run two waves of 64 x 128 per tile:
+  // two such workgroups share a CU with half the LDS fragment reads of four
+  // 64 x 64 waves each, which held those launches back (M = 512 N = 10240
+  // K = 5120: 39.6-41.1 -> 34.0-35.4 us, M = 1024 N = 5120 K = 17408
+  // 105-110 -> 91-92 us, M = 256 N = 34816 60-66 -> 57-59 us).  With at most
+  // one workgroup per CU, two waves would leave two SIMDs idle (M = 256
+  // N = 10240: 23.4-23.8 -> 27.3-28.0 us), so those keep four.
   auto small = [&](int n0, int n1, int s, void* work) {
     const size_t nt_off = static_cast<size_t>(n0) / 16;
-    return launch_cfg<128, 128, 2, 2, 2, true, false, AT>(a, lda, as, w + nt_off * KS * 1024,
-                                                          sc + nt_off * ((KS + 3) / 4) * 256, c + n0, ldc, M, n1 - n0,
-                                                          KS, 4, s, work, st);
+    const uint8_t* wn = w + nt_off * KS * 1024;
+    const uint8_t* sn = sc + nt_off * ((KS + 3) / 4) * 256;
+    const int wgs = ((M + 127) / 128) * ((n1 - n0 + 127) / 128) * s;
+    if (wgs > 256)
+      return launch_cfg<128, 128, 2, 1, 1, true, false, AT>(a, lda, as, wn, sn, c + n0, ldc, M, n1 - n0, KS, 4, s,
+                                                            work, st);
+    return launch_cfg<128, 128, 2, 2, 2, true, false, AT>(a, lda, as, wn, sn, c + n0, ldc, M, n1 - n0, KS, 4, s, work,
+                                                          st);
   };
   if (pl.n_mid > pl.n_main) {
     const int rc = small(pl.n_main, pl.n_mid, 1, nullptr);

@@ -171,7 +171,9 @@ def test_prefill_k_loop_keeps_mfmas_and_loads_interleaved():
         # the three unrolled steps of the loop each put min(half, loads) loads right after MFMAs
         assert interleaved >= 3 * min(half, dma), f"{name}: only {interleaved} MFMAs followed by a load"
         seen += 1
-    assert seen == 4, f"{seen} prefill instantiations found"
+    # 256x256 (4 waves), 128x128 as 4 waves of 64x64 and as 2 waves of 64x128, each
+    # for row-major and activation-tiled input
+    assert seen == 6, f"{seen} prefill instantiations found"
 
 
 def test_split_k_handoff_uses_device_scope_instructions():

@@ -120,7 +120,8 @@ def _w4_run(aq, asc, wp, e, out=None):
                                    (13, 2048, 17408), (65, 48, 384), (129, 176, 640), (200, 1024, 1024),
                                    (256, 1280, 5120), (300, 48, 17408), (5, 48, 12288),
                                    (16, 4096, 5120), (16, 208, 640),    # 16 rows: two tiles per wave
-                                   (7, 10240, 1024), (9, 10256, 640)])  # 5..15 rows, 640+ tiles: three per workgroup
+                                   (7, 10240, 1024), (9, 10256, 640),   # 5..15 rows, 640+ tiles: three per workgroup
+                                   (1100, 4112, 256)])  # 297 small tiles (> one per CU): two waves of 64 x 128
 def test_w4a8_full_oracle(M, N, K):
     aq, asc, wp, e = w4a8_inputs(8, M + N + K, M, N, K)
     got = host_bits16(_w4_run(aq, asc, wp, e))
