@@ -614,9 +614,10 @@ int launch_cfg(const uint8_t* a, int64_t lda, const float* as, const uint8_t* w,
 // tiles split K so that about 256 workgroups run, keeping at least 8 K steps
 // (1024 K) per split (measured with the batched split-K reduction: 80 tiles
 // run fastest with 3 splits, 160 tiles unsplit -- 512 workgroups were 10-20%
-// slower; 256 tiles, such as the column strips, run faster unsplit, except
-// over a long K: at K = 17408 a 256-tile strip split in two took the
-// M = 4096 N = 5120 launch from 284 to 269 us).
+// slower; 129 to 256 tiles, such as the column strips, run faster unsplit,
+// over a long K too since split launches of more than 256 workgroups take
+// the two-wave tile: M = 4096 N = 5120 K = 17408 243-253 -> 238-242 us,
+// M = 1024 N = 2560 K = 17408 61-63 -> 56-59 us against two splits).
 struct PrefillPlan {
   int n_main;   // columns [0, n_main) as 256x256 tiles (0: none)
   int n_mid;    // columns [n_main, n_mid) as unsplit 128x128 tiles, whole rounds of 512
@@ -647,7 +648,6 @@ PrefillPlan prefill_plan(int M, int N, int K) {
   if (ns > 0) {
     p.tiles = mts * ((ns + 127) / 128);
     if (p.tiles < 256) p.s = std::max(1, std::min(256 / p.tiles, KS / 8));
-    if (p.tiles <= 256 && KS >= 96) p.s = std::max(p.s, 2);  // one round of tiles over a long K
     p.s = std::min(p.s, 0x7FFFFFFF / KS);  // the split bounds are computed as KS * index in 32 bits
   }
   return p;

@@ -163,7 +163,7 @@ def test_prelayout_validation(blib):
     (256, 34816, 5120, 5, 32),      # 544 small tiles: 512 unsplit, the last 32 split five ways
     (500, 17456, 2048, 2, 36),      # 548 small tiles: 512 unsplit, the last 36 split in two
     (2048, 5120, 17408, 2, 128),    # 640 small tiles: 512 unsplit, the last 128 split in two (long K)
-    (4096, 5120, 17408, 2, 256),    # 256 large tiles + a 256-small-tile strip split in two (long K)
+    (4096, 5120, 17408, 1, 256),    # 256 large tiles + a 256-small-tile strip, unsplit (long K too)
     (2048, 17408, 5120, 2, 128),    # 1024 large tiles (4 rounds) + 128-tile strip split in two
     (2048, 10240, 5120, 1, 256),    # 256 large tiles + a 256-small-tile strip, unsplit
     (8192, 34816, 5120, 1, 0),      # 4352 large tiles (17 rounds), nothing else

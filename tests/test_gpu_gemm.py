@@ -159,7 +159,7 @@ def test_w4a8_large_tile_launch_full_oracle():
 
 def test_w4a8_down_projection_sampled():
     """M=4096 N=5120 K=17408 (the SiLU chain's down projection): large tiles
-    over 4096 columns plus a 256-tile column strip whose K is split in two."""
+    over 4096 columns plus an unsplit 256-tile column strip over K = 17408."""
     M, N, K = 4096, 5120, 17408
     aq, asc, wp, e = w4a8_inputs(5, 1, M, N, K)
     got = host_bits16(_w4_run(aq, asc, wp, e))
