@@ -414,7 +414,11 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
   } else if (d.mb == 1) {
     if (KS <= 20) set(2, 4, 1, 5);  // few K steps: fewer idle K-waves
     else if (wide_n && !long_k) set(1, 10, 1, 4);
-    else set(2, 8, 1, 5);
+    // 40 steps per workgroup as 8 waves of 10 rather than 16 of 5: half the
+    // waves to launch for the same loads in flight (M = 8 N = 5120: K = 5120
+    // 7.5 -> 7.3 us, K = 17408 24.0 -> 20.7 us; M = 8 N = 10240 K = 17408
+    // 40.6 -> 35.3 us; M = 16 K = 17408 unchanged)
+    else set(2, 4, 1, 10);
   } else if (mx) {
     set(8, 1, 1, 8);
   } else if (long_k) {
@@ -514,7 +518,7 @@ int launch_decode(bool mx, DecodeArgs& p, void* ws, hipStream_t st) {
     else if (d.mb == 4 && key == 801108) BS_DEC(true, 4, 8, 1, 1, 8);
     else return BS_ERR_SHAPE;
   } else {
-    if (d.mb == 1 && key == 208105) BS_DEC(false, 1, 2, 8, 1, 5);
+    if (d.mb == 1 && key == 204110) BS_DEC(false, 1, 2, 4, 1, 10);
     else if (d.mb == 1 && key == 204105) BS_DEC(false, 1, 2, 4, 1, 5);
     else if (d.mb == 1 && key == 110104) BS_DEC(false, 1, 1, 10, 1, 4);
     else if (d.mb == 2 && key == 402104) BS_DEC(false, 2, 4, 2, 1, 4);
