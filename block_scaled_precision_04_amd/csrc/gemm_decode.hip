@@ -412,8 +412,12 @@ DecodeCfg decode_cfg(int M, int N, int KS, bool mx) {
     else if (M >= 5 && N / 16 >= 640) set(3, 5, 1, 8);
     else set(1, 10, 1, 4);
   } else if (d.mb == 1) {
+    // wide N whose 40-step slice takes more than half the LDS (16 rows):
+    // 8 waves of 10 steps (M = 16, K = 5120: N = 10240 16.8 -> 15.4 us,
+    // N = 17408 26.1 -> 22.7 us; up to 12 rows 10 waves of 4 stay faster)
+    const bool slice_halves_lds = static_cast<size_t>(d.rs) * 40 * 128 > kMaxDecodeLds / 2;
     if (KS <= 20) set(2, 4, 1, 5);  // few K steps: fewer idle K-waves
-    else if (wide_n && !long_k) set(1, 10, 1, 4);
+    else if (wide_n && !long_k && !slice_halves_lds) set(1, 10, 1, 4);
     // 40 steps per workgroup as 8 waves of 10 rather than 16 of 5: half the
     // waves to launch for the same loads in flight (M = 8 N = 5120: K = 5120
     // 7.5 -> 7.3 us, K = 17408 24.0 -> 20.7 us; M = 8 N = 10240 K = 17408

@@ -49,7 +49,10 @@ def test_fp8_block_small_workload():
                                    (64, 1280, 2048), (3, 5120, 17408),
                                    # the 8-wave decode configurations: wide N (>= 512 tiles) and
                                    # long K (>= 96 steps) at 17..32 and 33..64 rows, ragged M
-                                   (17, 8192, 384), (50, 8192, 256), (20, 256, 12288), (47, 128, 12288)])
+                                   (17, 8192, 384), (50, 8192, 256), (20, 256, 12288), (47, 128, 12288),
+                                   # up to 16 rows past 20 K steps: 8 waves of 10 steps (ragged last
+                                   # split), and wide N at 12 / 16 rows (10 waves of 4 / 8 waves of 10)
+                                   (5, 640, 3200), (12, 8192, 2816), (16, 8192, 2816)])
 def test_fp8_block_edges(M, N, K):
     aq, asc, wq, wsc = fp8_block_inputs(9, M + N, M, N, K, outliers=True)
     got = _fp8_run(aq, asc, wq, wsc)
