@@ -110,8 +110,11 @@ def test_graph_replays_match_eager():
         _w4_call(8, 2048, 17408, 4),      # decode long-K configuration, split
         _w4_call(256, 1280, 5120, 5),     # small-tile prefill, K split
         _w4_call(4096, 5120, 1024, 6),    # large tiles + column strip
+        _w4_call(4096, 8192, 256, 10),    # 512 large tiles: two per workgroup
+        _w4_call(1100, 4112, 256, 11),    # 297 small tiles: two waves of 64 x 128 per tile
         _tiled_chain_call(300, 1280, 1024, 8),   # activation-tiled producer + GEMM (split small tiles)
-        _skinny_call(8, 256, 2048, 0),    # split over 4 workgroups
+        _skinny_call(8, 256, 2048, 0),    # up to 8 rows: one workgroup per column, no split
+        _skinny_call(16, 256, 2048, 12),  # split over 4 workgroups
         _skinny_call(64, 96, 5120, 9),    # split over 10 workgroups
     ] + _producer_calls()
     # eager reference (twice: the second call checks the workspaces were left ready)
