@@ -138,7 +138,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
     for (int i = 0; i < kAIters + kBIters; ++i) dma_piece(i, ks, buf);
     dma_scales(ks, buf);
   };
-  static_assert(kAIters + kBIters == kNB, "one load of the next stage per 16-column block");
+  // next-stage loads issued before a step's first MFMA, then two after each
+  // 16-column block's MFMAs until all are out (see the K loop)
+  constexpr int kDmaEarly = 2;
+  static_assert(kAIters + kBIters <= kDmaEarly + 2 * kNB, "the K loop issues every load of the next stage");
 
   // ---- fragment offsets within a stage.  Both operands hold K = 32*(l/16)
   // .. +31 of their row in lane l (the pre-layout's order; the pairing inside
@@ -173,11 +176,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
 
   for (int ks = 0; ks < KS; ++ks) {
     const int buf = ks & 1;
-    // The next stage's loads go out one per 16-column block, between the
-    // MFMAs, rather than as a burst before them: a burst of 17 loads per wave
-    // (136 per workgroup) backs up the load unit, and each wave stalls on it
-    // before its first MFMA.  After the last step they reload the last stage
-    // into the idle buffer (never read).
+    // The next stage's eight 16-byte loads per lane go out early in the step
+    // but not as one burst: two before the first MFMA, then two after each
+    // of the first three 16-column blocks' MFMAs, so they have most of the
+    // step to land before the wait that closes it.  A burst of all of them
+    // (plus the scales) before the MFMAs backs up the load unit and each
+    // wave stalls on it; one per block, spread over the whole step, leaves
+    // the last loads too little time (M=8192 N=5120 K=17408: one per block
+    // 752-763 us, this schedule 692-701, the burst 720; M=4096 N=10240
+    // K=5120 241-258 -> 225-235 us).  After the last step they reload the
+    // last stage into the idle buffer (never read).
     const int kn = min(ks + 1, KS - 1);
     dma_scales(kn, buf ^ 1);
     if (!live_n) {
@@ -199,6 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
                      *reinterpret_cast<const uint4*>(st + bfr + nb * 2048 + 1024));
       };
       v8i bcur = bfrag(0);
+#pragma unroll
+      for (int i = 0; i < kDmaEarly; ++i) dma_piece(i, kn, buf ^ 1);
       v4f t[kMB];
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
@@ -206,7 +216,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
         v4f tn[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) tn[mb] = mfma_group(bcur, af[mb]);
-        dma_piece(nb, kn, buf ^ 1);
+#pragma unroll
+        for (int i = kDmaEarly + 2 * nb; i < kDmaEarly + 2 * nb + 2 && i < kAIters + kBIters; ++i)
+          dma_piece(i, kn, buf ^ 1);
         if (nb > 0) {
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) acc[mb][nb - 1] += t[mb] * s[mb];
