@@ -295,21 +295,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_fp8_prefill(const uint8_t* __re
 }  // namespace
 
 // Whether the tiled kernel takes the call instead of the decode kernel, which
-// runs 64 rows per launch and streams the whole weight once per launch.  The
-// tiled kernel sweeps all of K in every 256x256 tile with no split, so below
-// 512 rows it has only ceil(M/256) * N/256 workgroups and its time is about
-// that of one tile's K sweep (75-79 us at K = 5120 for N = 5120 and 10240,
-// ~240 us at K = 17408).  Measured on MI355X against ceil(M/64) decode
-// launches (graph-replayed, pooled weights): at K = 5120 the tiled kernel is
-// faster from M = 384 (N = 5120: 81 -> 75 us; M = 448: 95 -> 76) and from
-// M = 256 at N = 10240 (83 -> 79; M = 448: 142 -> 79); at K = 17408 the
-// decode launches stay faster or equal up to M = 448.  Hence: from 512 rows
-// always, and below that when K has at most 64 steps and the decode
-// launches would stream at least 35840 columns' worth of weight rows
-// (ceil(M/64) * N >= 35840).
+// runs 64 rows per launch and streams the whole weight once per launch.  From
+// 512 rows always.  Up to 64 rows never: one decode launch streams the weight
+// once, and a 256x256 tile would waste most of its rows.  In between, a cost
+// model fitted to graph-replayed timings on MI355X (pooled weights) picks the
+// cheaper side.  The tiled kernel sweeps all of K in every tile with no
+// split, so it costs about 4 + 1.6 * K/128 us per round of 256 tiles (66-72
+// us at K = 5120, 210-222 us at K = 17408).  A 64-row decode launch costs
+// about 2 us plus 0.38 us per million weight bytes (13 / 21 / 35 us for
+// 26 / 52 / 89 MB).  Measured crossovers it reproduces: at N = K = 5120 the
+// decode launches win at M = 320 (63-64 against 66 us) and lose at 384
+// (76-77 against 66-67); at N = 10240, K = 5120 they win at 192 (63 against
+// 70) and lose at 256 (82 against 72); at N = 5120, K = 17408 they win at 256
+// (140 against 222), tie at 384 (209-211 against 209) and lose at 448 (244
+// against 213).
 bool bs_fp8_use_tiled(int M, int N, int K) {
   if (M >= 512) return true;
-  return K / 128 <= 64 && static_cast<int64_t>((M + 63) / 64) * N >= 35840;
+  if (M <= 64) return false;
+  const int64_t tiles = static_cast<int64_t>((M + 255) / 256) * ((N + 255) / 256);
+  // both estimates in units of 0.1 us
+  const int64_t tiled = (tiles + 255) / 256 * (40 + 16 * static_cast<int64_t>(K / 128));
+  const int64_t decode =
+      static_cast<int64_t>((M + 63) / 64) * (20 + static_cast<int64_t>(N) * static_cast<int64_t>(K) * 38 / 10000000);
+  return tiled < decode;
 }
 
 int bs_launch_fp8_block_prefill(const uint8_t* a, int64_t lda, const float* as, int64_t as_m, int64_t as_g,

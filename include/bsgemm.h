@@ -164,10 +164,12 @@ BS_API size_t bs_workspace_bytes(int op, int M, int N, int K);
  *          aligned, zeroed once) when that is non-zero: K split across
  *          workgroups; otherwise may be NULL.
  * Regimes: small M streams the weight (64 < M runs as consecutive 64-row
- * launches on the stream, all sharing ws); M >= 512, and from 129 rows up
- * when K <= 8192 and ceil(M/64) * N >= 35840 (where the repeated weight
- * stream costs more than the tiled kernel's K sweep), run the LDS-tiled
- * kernel (256x256 tiles), which needs no workspace.
+ * launches on the stream, all sharing ws); M >= 512, and 64 < M < 512 where
+ * a timing model puts the repeated weight stream above the tiled kernel's K
+ * sweep (about 4 + 1.6 * K/128 us per round of 256 tiles against
+ * ceil(M/64) * (2 + 0.38 * N*K/1e6) us), run the LDS-tiled kernel (256x256
+ * tiles), which needs no workspace; bs_workspace_bytes returns 0 exactly
+ * when the tiled kernel takes the call.
  * Needs M >= 1, N % 128 == 0, K % 128 == 0, K < 2^24, lda < 2^25,
  * 0 <= as_stride_m < 2^22, as_stride_g >= 0 (and, in the tiled regime,
  * lda < 2^24 and (N/128)*(K/128) < 2^30); a, c and w_pre 16-byte aligned,

@@ -60,11 +60,16 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(1, 8, 5120, 5120) == 0
     assert blib.bs_workspace_bytes(1, 8, 5120, 17408) > 0     # long K: split across workgroups
     assert blib.bs_workspace_bytes(1, 2048, 5120, 17408) == 0  # large M: the tiled kernel, no split
-    # 64 < M < 512: the tiled kernel only where the repeated weight stream costs more
-    assert blib.bs_workspace_bytes(1, 448, 5120, 5120) == 0    # 7 x 5120 >= 35840, K = 5120
-    assert blib.bs_workspace_bytes(1, 256, 10240, 5120) == 0   # 4 x 10240
-    assert blib.bs_workspace_bytes(1, 320, 5120, 5120) > 0     # 5 x 5120: decode launches
-    assert blib.bs_workspace_bytes(1, 448, 5120, 17408) > 0    # K = 17408: decode launches
+    # 64 < M < 512: the tiled kernel only where ceil(M/64) decode launches,
+    # each streaming the whole weight, cost more than its one K sweep
+    assert blib.bs_workspace_bytes(1, 448, 5120, 5120) == 0    # 7 weight streams
+    assert blib.bs_workspace_bytes(1, 384, 5120, 5120) == 0    # 6
+    assert blib.bs_workspace_bytes(1, 320, 5120, 5120) > 0     # 5: decode launches
+    assert blib.bs_workspace_bytes(1, 256, 10240, 5120) == 0   # 4 streams of a 52 MB weight
+    assert blib.bs_workspace_bytes(1, 192, 10240, 5120) > 0    # 3: decode launches
+    assert blib.bs_workspace_bytes(1, 448, 5120, 17408) == 0   # 7 streams of 89 MB against 136 K steps
+    assert blib.bs_workspace_bytes(1, 384, 5120, 17408) > 0    # 6: decode launches
+    assert blib.bs_workspace_bytes(1, 64, 40960, 5120) > 0     # up to 64 rows: always decode
     assert blib.bs_workspace_bytes(2, 8, 17408, 17408) > 0
     assert blib.bs_workspace_bytes(2, 8192, 34816, 5120) == 0   # tiled kernel on a full grid: no split
     assert blib.bs_workspace_bytes(2, 256, 5120, 17408) > 0     # small-M tiled kernel splits K

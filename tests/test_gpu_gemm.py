@@ -425,14 +425,15 @@ def test_fp8_block_prefill_edges(M, N, K, colmajor):
     checks.assert_gemm_close(got, ce, asum, f"fp8 block prefill edge M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K,tiled", [(448, 5120, 5120, True), (200, 10240, 5120, True),
-                                         (320, 5120, 5120, False), (448, 5120, 17408, False)])
+@pytest.mark.parametrize("M,N,K,tiled", [(448, 5120, 5120, True), (384, 5120, 5120, True),
+                                         (200, 10240, 5120, True), (320, 5120, 5120, False),
+                                         (448, 5120, 17408, True), (384, 5120, 17408, False)])
 def test_fp8_block_mid_m_routing(M, N, K, tiled):
-    """65 <= M < 512: the tiled kernel where ceil(M/64) decode launches would
-    stream the weight more often than it pays (K <= 8192 and
-    ceil(M/64) * N >= 35840), else the 64-row decode launches; the oracle
-    on a grid of the edge rows and columns plus random ones (about two per
-    16-row block and two per 256-column stripe)."""
+    """65 <= M < 512: the tiled kernel where its one K sweep per round of
+    tiles costs less than ceil(M/64) decode launches, each streaming the whole
+    weight (the library's timing model), else the 64-row decode launches; the
+    oracle on a grid of the edge rows and columns plus random ones (about two
+    per 16-row block and two per 256-column stripe)."""
     wsb = bs.lib().bs_workspace_bytes(bs.BS_OP_FP8_BLOCK, M, N, K)
     assert (wsb == 0) == tiled
     aq, asc, wq, wsc = fp8_block_inputs(12, M + N + K, M, N, K, outliers=True)
