@@ -505,8 +505,102 @@ __device__ __forceinline__ void prefill_tile(
       }
     }
   };
+  // The 256x256 tile's epilogue stages fp32 instead: its accumulators live in
+  // the accumulator registers, which the VALU cannot read, so scaling and
+  // converting them before the regroup costs a register read, a multiply and
+  // half a conversion per value on the VALU, one wave per SIMD, and the
+  // regroup is VALU-bound.  Here the accumulators go to LDS as they are
+  // (16-byte writes straight from the accumulator registers), half the
+  // tile's columns at a time (256 rows x 128 fp32 = 128 KiB), and the store
+  // pass reads each row's values back, multiplies by the row's scale,
+  // converts and stores: no register reads, no bf16 shuffling (the bench
+  // step 2.903-2.912 -> 2.890-2.894 ms, alternating the two builds on one
+  // box; bit-identical outputs).  Half h holds, for wave column wn, the tile
+  // columns wn*128 + 64h .. +63 at LDS columns wn*64 .. +63; 16-byte chunk k
+  // of a row sits at slot k ^ (row % 16), so the 16 rows of a write phase
+  // and the 16 lanes of a read phase (one row, chunks tid16 and tid16 + 16)
+  // each cover 16 distinct slots.  A lane stores its two 4-column pieces
+  // (8 bytes each; 16 lanes write 128 contiguous bytes of a row).
+  auto store_tile_f32 = [&]() {
+    if constexpr (IL) {
+      static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 2, "the fp32-staged epilogue is the 256x256 tile's");
+      static_assert(BM * (BN / 2) * 4 <= STAGES * C::kStage, "half the fp32 tile must fit the stage buffers");
+      constexpr int kRowBytes = (BN / 2) * 4;           // 512
+      constexpr int kPasses = BM / 16, kBatch = 8;      // 16 rows per pass (16 lanes per row)
+      const int tid16 = tid & 15, rsub = tid >> 4;      // rows rsub, rsub + 16, ...: row % 16 == rsub
+      const bool whole = m0 + BM <= M && n0 + BN <= N;
+      // this lane's two 16-byte chunks of a row in the store pass: chunk tid16
+      // (LDS columns 4 * tid16 .. +3, wave column 0) and chunk tid16 + 16
+      // (columns 64 + 4 * tid16 .., wave column 1); the 16 lanes of a read
+      // phase cover the 16 slots of one 256-byte line
+      const int o0 = (tid16 ^ rsub) << 4, o1 = ((tid16 + 16) ^ rsub) << 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // every wave is done with the stage buffers (h = 0) / with half 0 (h = 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < C::kTM; ++q) {
+          const int r = arow[q];
+          uint8_t* rowp = lds + r * kRowBytes;
+          const int x = r & 15;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int k = wn * 16 + 8 * pp + 2 * j + (l >> 5);
+              const v16f& av = acc[2 * h + pp][q];
+              *reinterpret_cast<float4*>(rowp + ((k ^ x) << 4)) =
+                  make_float4(av[4 * j + 0], av[4 * j + 1], av[4 * j + 2], av[4 * j + 3]);
+            }
+        }
+        __syncthreads();
+        // LDS columns c < 64 are tile columns c + 64h, the others c + 64h + 64
+        const int ncol = 4 * tid16 + 64 * h;   // and ncol + 128
+        const uint8_t* rd = lds + rsub * kRowBytes;
+        auto row_out = [&](int pass) {
+          const uint8_t* rp = rd + pass * 16 * kRowBytes;
+          const float4 u = *reinterpret_cast<const float4*>(rp + o0);
+          const float4 v = *reinterpret_cast<const float4*>(rp + o1);
+          const float sc = s_tok[pass * 16 + rsub];
+          return make_uint4(bf16x2_rne(u.x * sc, u.y * sc), bf16x2_rne(u.z * sc, u.w * sc),
+                            bf16x2_rne(v.x * sc, v.y * sc), bf16x2_rne(v.z * sc, v.w * sc));
+        };
+        if (whole) {
+          // scalar row stride; a batch's LDS reads are issued before its stores
+          uint16_t* dst = c + static_cast<int64_t>(m0 + rsub) * ldc + n0 + ncol;
+          const int64_t rstep = 16 * ldc;
+#pragma unroll
+          for (int b0 = 0; b0 < kPasses; b0 += kBatch) {
+            uint4 o[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) o[i] = row_out(b0 + i);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+              st_stream8(reinterpret_cast<uint2*>(dst + (b0 + i) * rstep), o[i].x, o[i].y);
+              st_stream8(reinterpret_cast<uint2*>(dst + (b0 + i) * rstep + 128), o[i].z, o[i].w);
+            }
+          }
+        } else {
+          // N % 16 == 0: each 4-column piece is all inside or all outside
+          const bool n_ok0 = n0 + ncol < N, n_ok1 = n0 + ncol + 128 < N;
+#pragma unroll 4
+          for (int pass = 0; pass < kPasses; ++pass) {
+            const int r = pass * 16 + rsub;
+            const uint4 o = row_out(pass);
+            if (m0 + r < M) {
+              uint16_t* dst = c + static_cast<int64_t>(m0 + r) * ldc + n0 + ncol;
+              if (n_ok0) st_stream8(reinterpret_cast<uint2*>(dst), o.x, o.y);
+              if (n_ok1) st_stream8(reinterpret_cast<uint2*>(dst + 128), o.z, o.w);
+            }
+          }
+        }
+      }
+    }
+  };
   if (!SPLIT || S == 1) {
-    store_tile();
+    if constexpr (IL) store_tile_f32();
+    else store_tile();
     return;
   }
   // Split K: the fp32 partial tile in MFMA fragment order (element r of lane
