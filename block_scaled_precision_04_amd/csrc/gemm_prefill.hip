@@ -505,38 +505,45 @@ __device__ __forceinline__ void prefill_tile(
       }
     }
   };
-  // The 256x256 tile's epilogue stages fp32 instead: its accumulators live in
-  // the accumulator registers, which the VALU cannot read, so scaling and
-  // converting them before the regroup costs a register read, a multiply and
-  // half a conversion per value on the VALU, one wave per SIMD, and the
-  // regroup is VALU-bound.  Here the accumulators go to LDS as they are
-  // (16-byte writes straight from the accumulator registers), half the
-  // tile's columns at a time (256 rows x 128 fp32 = 128 KiB), and the store
-  // pass reads each row's values back, multiplies by the row's scale,
-  // converts and stores: no register reads, no bf16 shuffling (the bench
-  // step 2.903-2.912 -> 2.890-2.894 ms, alternating the two builds on one
-  // box; bit-identical outputs).  Half h holds, for wave column wn, the tile
-  // columns wn*128 + 64h .. +63 at LDS columns wn*64 .. +63; 16-byte chunk k
+  // The tiles whose accumulators live in the accumulator registers (256x256,
+  // and 128x128 as two waves of 64x128) stage fp32 instead: the VALU cannot
+  // read those registers, so scaling and converting before the regroup
+  // costs a register read, a multiply and half a conversion per value on
+  // the VALU, one wave per SIMD, and the regroup is VALU-bound.  Here the
+  // accumulators go to LDS as they are (16-byte writes straight from the
+  // accumulator registers), 128 columns of the tile at a time (BM rows x 128
+  // fp32: two passes of 128 KiB for 256x256, one of 64 KiB for 128x128), and
+  // the store pass reads each row's values back, multiplies by the row's
+  // scale, converts and stores: no register reads, no bf16 shuffling (bench
+  // step with the 256x256 tile so: 2.903-2.912 -> 2.890-2.894 ms,
+  // alternating the two builds on one box; bit-identical outputs).  Column
+  // pass h holds, for wave column wn, the wave's kW-column slice h (kW = 64
+  // for 256x256, 128 for 128x128) at LDS columns wn*kW ..; 16-byte chunk k
   // of a row sits at slot k ^ (row % 16), so the 16 rows of a write phase
   // and the 16 lanes of a read phase (one row, chunks tid16 and tid16 + 16)
-  // each cover 16 distinct slots.  A lane stores its two 4-column pieces
-  // (8 bytes each; 16 lanes write 128 contiguous bytes of a row).
+  // each cover 16 distinct slots.  A lane stores two 4-column pieces (8
+  // bytes each; 16 lanes write 128 contiguous bytes of a row).
+  constexpr bool kF32Epi =
+      (BM == 256 && BN == 256 && WM == 2 && WN == 2) || (BM == 128 && BN == 128 && WM == 2 && WN == 1);
   auto store_tile_f32 = [&]() {
-    if constexpr (IL) {
-      static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 2, "the fp32-staged epilogue is the 256x256 tile's");
-      static_assert(BM * (BN / 2) * 4 <= STAGES * C::kStage, "half the fp32 tile must fit the stage buffers");
-      constexpr int kRowBytes = (BN / 2) * 4;           // 512
-      constexpr int kPasses = BM / 16, kBatch = 8;      // 16 rows per pass (16 lanes per row)
-      const int tid16 = tid & 15, rsub = tid >> 4;      // rows rsub, rsub + 16, ...: row % 16 == rsub
+    if constexpr (kF32Epi) {
+      constexpr int kPassN = BN / 128;                 // column passes
+      constexpr int kPP = C::kTN / kPassN;             // a wave's 32-column blocks per pass
+      constexpr int kW = kPP * 32;                     // a wave's columns per pass
+      static_assert(WN * kW == 128 && C::kTN % kPassN == 0, "128 staged columns per pass");
+      static_assert(BM * 128 * 4 <= STAGES * C::kStage, "a column pass must fit the stage buffers");
+      constexpr int kRowBytes = 128 * 4;
+      constexpr int kRows = C::kThreads / 16;          // rows per store pass (16 lanes per row)
+      constexpr int kPasses = BM / kRows, kBatch = 8;
+      static_assert(kPasses % kBatch == 0, "store batch shape");
+      // tile-column distance of LDS column 64 + x from LDS column x (x < 64)
+      constexpr int kDelta = kW == 64 ? BN / WN : 64;
+      const int tid16 = tid & 15, rsub = tid >> 4;
       const bool whole = m0 + BM <= M && n0 + BN <= N;
-      // this lane's two 16-byte chunks of a row in the store pass: chunk tid16
-      // (LDS columns 4 * tid16 .. +3, wave column 0) and chunk tid16 + 16
-      // (columns 64 + 4 * tid16 .., wave column 1); the 16 lanes of a read
-      // phase cover the 16 slots of one 256-byte line
-      const int o0 = (tid16 ^ rsub) << 4, o1 = ((tid16 + 16) ^ rsub) << 4;
+      wait_vm<0>();
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // every wave is done with the stage buffers (h = 0) / with half 0 (h = 1)
+      for (int h = 0; h < kPassN; ++h) {
+        // every wave is done with the stage buffers (h = 0) / with pass h - 1
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();
 #pragma unroll
@@ -545,31 +552,32 @@ __device__ __forceinline__ void prefill_tile(
           uint8_t* rowp = lds + r * kRowBytes;
           const int x = r & 15;
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp)
+          for (int pp = 0; pp < kPP; ++pp)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int k = wn * 16 + 8 * pp + 2 * j + (l >> 5);
-              const v16f& av = acc[2 * h + pp][q];
+              const int k = wn * (kW / 4) + 8 * pp + 2 * j + (l >> 5);
+              const v16f& av = acc[h * kPP + pp][q];
               *reinterpret_cast<float4*>(rowp + ((k ^ x) << 4)) =
                   make_float4(av[4 * j + 0], av[4 * j + 1], av[4 * j + 2], av[4 * j + 3]);
             }
         }
         __syncthreads();
-        // LDS columns c < 64 are tile columns c + 64h, the others c + 64h + 64
-        const int ncol = 4 * tid16 + 64 * h;   // and ncol + 128
-        const uint8_t* rd = lds + rsub * kRowBytes;
+        // LDS column 4 * tid16 is tile column 4 * tid16 + h * kW; LDS column
+        // 64 + 4 * tid16 is kDelta further on
+        const int ncol = 4 * tid16 + h * kW;
         auto row_out = [&](int pass) {
-          const uint8_t* rp = rd + pass * 16 * kRowBytes;
-          const float4 u = *reinterpret_cast<const float4*>(rp + o0);
-          const float4 v = *reinterpret_cast<const float4*>(rp + o1);
-          const float sc = s_tok[pass * 16 + rsub];
+          const int r = pass * kRows + rsub, x = r & 15;
+          const uint8_t* rp = lds + r * kRowBytes;
+          const float4 u = *reinterpret_cast<const float4*>(rp + ((tid16 ^ x) << 4));
+          const float4 v = *reinterpret_cast<const float4*>(rp + (((tid16 + 16) ^ x) << 4));
+          const float sc = s_tok[r];
           return make_uint4(bf16x2_rne(u.x * sc, u.y * sc), bf16x2_rne(u.z * sc, u.w * sc),
                             bf16x2_rne(v.x * sc, v.y * sc), bf16x2_rne(v.z * sc, v.w * sc));
         };
         if (whole) {
           // scalar row stride; a batch's LDS reads are issued before its stores
           uint16_t* dst = c + static_cast<int64_t>(m0 + rsub) * ldc + n0 + ncol;
-          const int64_t rstep = 16 * ldc;
+          const int64_t rstep = kRows * ldc;
 #pragma unroll
           for (int b0 = 0; b0 < kPasses; b0 += kBatch) {
             uint4 o[kBatch];
@@ -578,20 +586,20 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) {
               st_stream8(reinterpret_cast<uint2*>(dst + (b0 + i) * rstep), o[i].x, o[i].y);
-              st_stream8(reinterpret_cast<uint2*>(dst + (b0 + i) * rstep + 128), o[i].z, o[i].w);
+              st_stream8(reinterpret_cast<uint2*>(dst + (b0 + i) * rstep + kDelta), o[i].z, o[i].w);
             }
           }
         } else {
           // N % 16 == 0: each 4-column piece is all inside or all outside
-          const bool n_ok0 = n0 + ncol < N, n_ok1 = n0 + ncol + 128 < N;
+          const bool n_ok0 = n0 + ncol < N, n_ok1 = n0 + ncol + kDelta < N;
 #pragma unroll 4
           for (int pass = 0; pass < kPasses; ++pass) {
-            const int r = pass * 16 + rsub;
+            const int r = pass * kRows + rsub;
             const uint4 o = row_out(pass);
             if (m0 + r < M) {
               uint16_t* dst = c + static_cast<int64_t>(m0 + r) * ldc + n0 + ncol;
               if (n_ok0) st_stream8(reinterpret_cast<uint2*>(dst), o.x, o.y);
-              if (n_ok1) st_stream8(reinterpret_cast<uint2*>(dst + 128), o.z, o.w);
+              if (n_ok1) st_stream8(reinterpret_cast<uint2*>(dst + kDelta), o.z, o.w);
             }
           }
         }
@@ -599,7 +607,7 @@ __device__ __forceinline__ void prefill_tile(
     }
   };
   if (!SPLIT || S == 1) {
-    if constexpr (IL) store_tile_f32();
+    if constexpr (kF32Epi) store_tile_f32();
     else store_tile();
     return;
   }
@@ -641,7 +649,8 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[p][q][r] = tot[(p * C::kTM + q) * 16 + r];
   }
-  store_tile();
+  if constexpr (kF32Epi) store_tile_f32();
+  else store_tile();
   if (tid == 0) __hip_atomic_store(&counters[bx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
