@@ -298,6 +298,26 @@ def test_w4a8_prefill_out_ldc_not_multiple_of_8():
     checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 ldc 4 mod 8")
 
 
+@pytest.mark.parametrize("M,N,K", [(4000, 4240, 512),   # 16 x 16 large tiles + a 144-column strip
+                                   (2000, 2544, 512)])  # 320 two-wave small tiles, ragged rows and columns
+def test_w4a8_fp32_staged_epilogue_ldc_4_mod_8(M, N, K):
+    """The tiles that stage fp32 accumulators in LDS (256x256, and 128x128 as
+    two waves) store 8-byte pieces; here into a view whose leading dimension
+    is 4 mod 8 elements, with a guard below and beside it.  Nothing outside the
+    view changes and every element matches the oracle."""
+    aq, asc, wp, e = w4a8_inputs(8, 17 + M, M, N, K)
+    big = torch.full((M + 1, N + 44), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[0:M, 8:8 + N]    # first row 16-byte aligned, the rows after it 8 mod 16
+    assert view.stride(0) % 8 == 4
+    _w4_run(aq, asc, wp, e, out=view)
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[0:M, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, f"w4a8 fp32-staged ldc 4 mod 8 M={M} N={N}")
+
+
 def test_w4a8_large_tiles_strided_out():
     """The large-tile launch and its column strip writing into a strided view:
     M=4000 (last 256-row tile 160 rows deep), N=4240 -> 16 x 16 large tiles
