@@ -121,13 +121,15 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x, 
   if (threadIdx.x == 0) __hip_atomic_store(&counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Up to 8 rows and K <= 2048: one output column per workgroup over the whole
-// of K, dot products on the VALU (v_dot2 over packed bf16 pairs, fp32 sums),
-// so there is no split-K hand-off (M = 6 / 8, W[256, 2048]: 4.46-4.64 ->
-// 3.98-4.01 us graph-replayed over pooled weights, 7.3-7.4 -> 6.5-6.7 us
-// inside the bench step).  Past that each workgroup streams too much of the
-// activation: W[96, 5120] at 8 rows ran 0.2-0.4 us slower inside the bench
-// step (3% faster alone), and at 16 rows W[256, 2048] went from 4.7 to 5.8 us.  Thread t takes the 16-byte chunks t, t + T, ... of
+// Up to 32 rows and K <= 2048: one output column and up to 8 rows per
+// workgroup (grid (N, ceil(M/8))) over the whole of K, dot products on the
+// VALU (v_dot2 over packed bf16 pairs, fp32 sums), so there is no split-K
+// hand-off (graph-replayed over pooled weights, W[256, 2048]: M = 6 / 8
+// 4.46-4.64 -> 3.98-4.01 us, M = 16 5.04-5.10 -> 4.37-4.44, M = 32 5.77 ->
+// 5.21-5.25).  Past that each workgroup streams too much of the activation
+// (M * K * 2 bytes over the row groups): M = 64 went from 7.2 to 7.7 us, and
+// W[96, 5120] at 8 rows ran 0.2-0.4 us slower inside the bench step (3%
+// faster alone), so those keep the split MFMA form.  Thread t takes the 16-byte chunks t, t + T, ... of
 // the weight row and of each activation row; all NCH chunks' loads are
 // issued before any arithmetic (chunk indices past K re-read the last chunk
 // and are zeroed afterwards), then each row's sum goes through a wave
@@ -138,6 +140,10 @@ __global__ __launch_bounds__(T) void k_skinny_dot(const uint16_t* __restrict__ x
   constexpr int kW = T / 64;
   __shared__ float red[kW][MR];
   const int n = blockIdx.x;
+  // blockIdx.y takes rows 8y .. 8y + 7 (at most MR)
+  x += static_cast<size_t>(blockIdx.y) * MR * K;
+  c += static_cast<size_t>(blockIdx.y) * MR * N;
+  M -= blockIdx.y * MR;
   const int t = threadIdx.x, wave = t >> 6, l = t & 63;
   const int nch = K >> 3;
   const uint4* wr = reinterpret_cast<const uint4*>(w + static_cast<size_t>(n) * K);
@@ -188,7 +194,7 @@ int bs_skinny_ksplit(int K) { return ((K + kChunk - 1) / kChunk + kWaves - 1) / 
 
 namespace {
 // whether the VALU form (one column per workgroup, no split) takes the call
-bool skinny_dot(int M, int K) { return M <= 8 && K <= 2048; }
+bool skinny_dot(int M, int K) { return M <= 32 && K <= 2048; }
 }  // namespace
 
 namespace {
@@ -208,7 +214,7 @@ int bs_launch_skinny(const uint16_t* x, const uint16_t* w, uint16_t* c, int M, i
                      hipStream_t st) {
   if (skinny_dot(M, K)) {
     // K <= 2048: at most 256 16-byte chunks per row, one per thread
-    k_skinny_dot<8, 256, 1><<<dim3(N), dim3(256), 0, st>>>(x, w, c, M, N, K);
+    k_skinny_dot<8, 256, 1><<<dim3(N, (M + 7) / 8), dim3(256), 0, st>>>(x, w, c, M, N, K);
     return bs_launch_status();
   }
   const int ks = bs_skinny_ksplit(K);

@@ -219,9 +219,10 @@ BS_API int bsgemm_w4a8_mxfp4_atiled(const void* a_tiled, const float* a_scale, c
  *   C[m,n] = bf16( sum_k x[m,k] * w[n,k] ), fp32 accumulation.
  * x: bf16 [M, K]; w: bf16 [N, K]; c: bf16 [M, N]; all contiguous row-major,
  * 16-byte aligned.  1 <= M <= 64, N % 16 == 0, K >= 32, K % 32 == 0 (K past
- * the last multiple of 128 runs as a partial chunk).  Up to 8 rows with
- * K <= 2048, one workgroup per output column walks all of K and no workspace
- * is used; otherwise K is split across workgroups and ws must hold
+ * the last multiple of 128 runs as a partial chunk).  Up to 32 rows with
+ * K <= 2048, one workgroup per output column and group of 8 rows walks all
+ * of K and no workspace is used; otherwise K is split across workgroups and
+ * ws must hold
  * bs_workspace_bytes(BS_OP_BF16_SKINNY, ...) (0 in the first case). */
 BS_API int gemm_bf16_skinny(const void* x, const void* w, void* c, int M, int N, int K, void* ws,
                             size_t ws_bytes, bs_stream_t stream);

@@ -76,7 +76,8 @@ def test_sizes(blib):
     assert blib.bs_workspace_bytes(1, 8, 100, 5120) == 0      # N % 128 != 0 -> 0
     assert blib.bs_workspace_bytes(3, 8, 256, 2048) == 0      # skinny, 8 rows, K <= 2048: one workgroup per column
     assert blib.bs_workspace_bytes(3, 8, 96, 5120) > 0        # longer K: split
-    assert blib.bs_workspace_bytes(3, 16, 256, 2048) > 0      # 16 rows: split
+    assert blib.bs_workspace_bytes(3, 32, 256, 2048) == 0     # up to 32 rows: workgroups per column and 8 rows
+    assert blib.bs_workspace_bytes(3, 33, 256, 2048) > 0      # 33 rows: split
     assert blib.bs_workspace_bytes(3, 65, 96, 5120) == 0     # M out of range -> 0
 
 

@@ -406,9 +406,11 @@ def test_skinny_workload(case):
                                    # alone (K = 32, 96) and after whole ones, split and unsplit
                                    (8, 16, 32), (3, 32, 96), (16, 64, 160), (33, 96, 2080), (64, 48, 5024),
                                    (8, 96, 5216),
-                                   # up to 8 rows, one workgroup per column up to K = 2048 (all chunk
-                                   # slots used at 2048, idle ones below); just past it, the split form
-                                   (8, 64, 2048), (2, 16, 1056), (6, 48, 2080), (8, 32, 8192)])
+                                   # up to 32 rows, one workgroup per column and 8 rows up to K = 2048
+                                   # (all chunk slots used at 2048, idle ones below; a partial last row
+                                   # group); just past either limit, the split form
+                                   (8, 64, 2048), (2, 16, 1056), (6, 48, 2080), (8, 32, 8192),
+                                   (27, 32, 1024), (32, 16, 2048), (33, 16, 2048)])
 def test_skinny_edges(M, N, K):
     g = synth.rng(M * 1000 + N + K)
     x = synth.bf16_normal(g, (M, K), 1.0)
