@@ -318,6 +318,28 @@ def test_w4a8_fp32_staged_epilogue_ldc_4_mod_8(M, N, K):
     checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, f"w4a8 fp32-staged ldc 4 mod 8 M={M} N={N}")
 
 
+def test_w4a8_large_tiles_and_unsplit_strip_full_oracle():
+    """Large tiles and an unsplit column strip of small tiles: M=2000 (last
+    256-row tile 208 rows deep, last 128-row tile 80), N=8496 -> 8 x 32 large
+    tiles over 8192 columns plus a 304-column strip of 16 x 3 small tiles
+    (the last 48 columns wide), K=1024 (too short to split), into a view
+    whose leading dimension is 4 mod 8, with a guard; every element against
+    the oracle."""
+    M, N, K = 2000, 8496, 1024
+    aq, asc, wp, e = w4a8_inputs(8, 21, M, N, K)
+    assert bs.lib().bs_workspace_bytes(bs.BS_OP_W4A8_MXFP4, M, N, K) == 0
+    big = torch.full((M + 1, N + 44), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[0:M, 8:8 + N]
+    assert view.stride(0) % 8 == 4
+    _w4_run(aq, asc, wp, e, out=view)
+    host = big.float().cpu().numpy()
+    mask = np.ones(host.shape, bool)
+    mask[0:M, 8:8 + N] = False
+    assert np.all(host[mask] == -7.0)
+    _, ce, asum = gemm.w4a8_mxfp4_gemm(aq, asc, wp, e)
+    checks.assert_gemm_close(host_bits16(view.contiguous()), ce, asum, "w4a8 large tiles + unsplit strip")
+
+
 def test_w4a8_large_tiles_strided_out():
     """The large-tile launch and its column strip writing into a strided view:
     M=4000 (last 256-row tile 160 rows deep), N=4240 -> 16 x 16 large tiles
