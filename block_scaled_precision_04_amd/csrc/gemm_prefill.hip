@@ -25,11 +25,13 @@
 // 16 distinct 16-byte slots of a 256-byte line; the fragment reads take one
 // chunk of 16 consecutive rows, two rows per 256 bytes, and the swizzle by
 // (row / 2) % 8 gives each row pair the eight slots (measured: the swizzle by
-// row % 8 served these reads in two passes).  The per-token activation scale multiplies the accumulator in the
-// epilogue, then bf16 RNE and store.  The first MFMA operand is the weight
-// (rows = n), the second the activation (rows = m), so each lane holds four
-// consecutive n of one m; the epilogue regroups them in LDS into whole output
-// rows before storing.  Which tile size runs where (and the
+// row % 8 served these reads in two passes).  The per-token activation
+// scale multiplies the accumulator in the epilogue, then bf16 RNE and store.
+// The first MFMA operand is the weight (rows = n), the second the
+// activation (rows = m), so each lane holds four consecutive n of one m; the
+// epilogue regroups them in LDS into whole output rows before storing (as
+// bf16 where the accumulators are ordinary registers, as fp32 straight from
+// the accumulator registers otherwise).  Which tile size runs where (and the
 // column strip that avoids a partial last round of large tiles) is decided by
 // prefill_plan below.
 //
