@@ -432,7 +432,7 @@ def test_skinny_workload(case):
                                    # (all chunk slots used at 2048, idle ones below; a partial last row
                                    # group); just past either limit, the split form
                                    (8, 64, 2048), (2, 16, 1056), (6, 48, 2080), (8, 32, 8192),
-                                   (27, 32, 1024), (32, 16, 2048), (33, 16, 2048)])
+                                   (27, 32, 1024), (32, 16, 2048), (33, 16, 2048), (20, 48, 96)])
 def test_skinny_edges(M, N, K):
     g = synth.rng(M * 1000 + N + K)
     x = synth.bf16_normal(g, (M, K), 1.0)
